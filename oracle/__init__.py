@@ -1,0 +1,5 @@
+"""CPU oracle of the LatentMoE layer forward. Test infrastructure only: it may be
+imported by the tests, the smoke check and the benchmark's CPU-baseline leg, and
+by nothing on the library path."""
+from .moe_oracle import *  # noqa: F401,F403
+from .moe_oracle import __all__  # noqa: F401
