@@ -1,0 +1,153 @@
+/*
+ * moe_api.h -- C ABI of the MI355X (gfx950) LatentMoE layer forward.
+ *
+ * The layer (the "Nemotron 3 Ultra 架构 QA" page, CH5 Q5.1-Q5.8 with the
+ * activation of Q2.6; the Nemotron-3 Ultra architecture walkthrough on
+ * 2kiu.com, section "LatentMoE 层"):
+ *
+ *   l   = x . W_r^T                 fp32 router logits over the uncompressed x   (QA Q5.2)
+ *   s   = sigmoid(l)                independent per expert                       (QA Q5.2)
+ *   c   = s + e_score_correction_bias, top-K experts by c                        (QA Q5.2, Q5.3)
+ *   g   = routed_scaling * s[chosen] / sum(s[chosen])                            (walkthrough; QA Q5.8)
+ *   z   = x . W_fc1^T               fc1_latent_proj, H -> L                       (QA Q5.1)
+ *   y_e = W_down[e] . relu(W_up[e] . z)^2, non-gated expert MLP, L -> I -> L      (QA Q2.6, Q5.5, Q5.6)
+ *   y_lat = sum_k g_k * y_{e_k}     gate applied to each expert output, summed    (QA Q5.5 point 3)
+ *   out = y_lat . W_fc2^T + W_sd . relu(W_su . x)^2                               (QA Q5.1, Q5.7)
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" point to GPU memory on the current HIP device;
+ *    the caller allocates, owns and frees every buffer, including the
+ *    workspace. The library never allocates device memory and keeps no state
+ *    between calls.
+ *  - bf16 tensors are passed as uint16_t bit patterns (IEEE binary32 upper
+ *    halves). All matrices are row-major; every weight is [out, in] (the
+ *    reduction index is contiguous).
+ *  - Calls are asynchronous on `stream` (0 = the null stream): no host
+ *    synchronisation, no host<->device copy. The return code reports argument
+ *    validation and launch errors; faults inside kernels surface at the
+ *    caller's next synchronisation.
+ *  - Nothing throws across the ABI. Results are deterministic: a call with the
+ *    same inputs gives bit-identical outputs (no floating-point atomics).
+ *  - A token's K experts are reported in ascending expert index; equal choice
+ *    scores are resolved toward the lower expert index.
+ */
+#ifndef MOE_API_H
+#define MOE_API_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Sizes of one forward. T tokens, H hidden, L latent (moe_latent_size), E routed
+ * experts, I expert intermediate, K experts per token, Is shared-expert
+ * intermediate; routed_scaling multiplies the renormalised gates (5.0 in the
+ * stated model, QA Q5.8). Host struct. */
+typedef struct moe_dims {
+  int32_t T, H, L, E, I, K, Is;
+  float routed_scaling;
+} moe_dims;
+
+/* Weights, all device pointers, all [out, in] row-major.
+ *   w_router  [E, H]    fp32   router weight (QA Q5.2 reads it as fp32)
+ *   corr_bias [E]       fp32   e_score_correction_bias (QA Q5.3, kept in fp32)
+ *   w_fc1     [L, H]    bf16   fc1_latent_proj
+ *   w_up      [E, I, L] bf16   expert up projections (QA Q5.6 3-D layout)
+ *   w_down    [E, L, I] bf16   expert down projections
+ *   w_fc2     [H, L]    bf16   fc2_latent_proj
+ *   w_sh_up   [Is, H]   bf16   shared expert up
+ *   w_sh_down [H, Is]   bf16   shared expert down */
+typedef struct moe_weights {
+  const float* w_router;
+  const float* corr_bias;
+  const uint16_t* w_fc1;
+  const uint16_t* w_up;
+  const uint16_t* w_down;
+  const uint16_t* w_fc2;
+  const uint16_t* w_sh_up;
+  const uint16_t* w_sh_down;
+} moe_weights;
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,      /* null pointer, non-positive size, K > E, bad C */
+  MOE_ERR_UNSUPPORTED = -2,  /* H, L, I or Is not a multiple of 64; E > 1024; K > 64 */
+  MOE_ERR_WORKSPACE = -3,    /* workspace null, too small or not 256-byte aligned */
+  MOE_ERR_HIP = -4           /* a HIP launch failed */
+};
+
+/* Byte offsets, inside the moe_forward workspace, of the intermediate tensors
+ * it leaves behind (valid after the stream reaches the end of the call):
+ *   idx [T,K] int32, gate [T,K] fp32, gap [T] fp32, offsets [E+1] int32,
+ *   row_token [T*K] int32, slot_row [T*K] int32 (index t*K+k),
+ *   z [T,L] bf16, h [T*K,I] bf16, y [T*K,L] bf16, y_lat [T,L] bf16, hs [T,Is] bf16.
+ * Returns MOE_OK or MOE_ERR_INVALID. */
+typedef struct moe_ws_layout {
+  size_t idx, gate, gap, offsets, row_token, slot_row, z, h, y, y_lat, hs, total;
+} moe_ws_layout;
+
+/* Router: fp32 logits, sigmoid, bias-adjusted top-K, renormalised and scaled gates.
+ * (QA Q5.2, Q5.3, Q5.8; walkthrough "路由与共享专家"). Reads T, H, E, K and
+ * routed_scaling of dims (the other fields are ignored).
+ *   x         device [T,H] bf16
+ *   w_router  device [E,H] fp32;  corr_bias device [E] fp32
+ *   topk_idx  device [T,K] int32 out: chosen experts, ascending per token
+ *   topk_gate device [T,K] fp32 out: routed_scaling * s / sum(s) over the chosen
+ *   topk_gap  device [T]   fp32 out, may be NULL: c_(K) - c_(K+1), the margin
+ *             between the last chosen and the first unchosen choice score in
+ *             descending order (+inf when K == E)
+ *   ws        device workspace of at least moe_route_workspace_bytes(dims) bytes,
+ *             256-byte aligned
+ * The logits are accumulated in fp32 from exact bf16 x fp32 products (the fp32
+ * weight is split into three bf16 parts); only the summation order differs
+ * from an exact fp32 dot product. */
+size_t moe_route_workspace_bytes(const moe_dims* dims);
+int moe_route(const moe_dims* dims, const uint16_t* x, const float* w_router,
+              const float* corr_bias, int32_t* topk_idx, float* topk_gate, float* topk_gap,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Permutation: group the T*K (token, slot) pairs by expert, tokens ascending within
+ * an expert -- the rows a loop over the hit experts gathers (QA Q5.6) -- and
+ * gather rows of `src` into that order. Reads T, E, K of dims (the other
+ * fields are ignored). Entries of topk_idx outside [0,E) are skipped and their
+ * slot_row is set to -1 (rows past the valid count are then left unwritten).
+ *   topk_idx       device [T,K] int32, values in [0,E), distinct within a token
+ *   src            device [T,C] bf16 (may be NULL together with dst: maps only)
+ *   C              row length of src/dst in elements, a multiple of 8
+ *   dst            device [T*K, C] bf16 out: dst[r] = src[row_token[r]]
+ *   expert_offsets device [E+1] int32 out: rows of expert e are [off[e], off[e+1])
+ *   row_token      device [T*K] int32 out: token of permuted row r
+ *   slot_row       device [T*K] int32 out: permuted row of slot (t,k), index t*K+k
+ *   ws             device workspace, >= moe_permute_workspace_bytes(dims), 256-aligned
+ * Bit-exact and deterministic (no order-dependent atomics). */
+size_t moe_permute_workspace_bytes(const moe_dims* dims);
+int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* src, int32_t C,
+                uint16_t* dst, int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Whole layer forward (QA Q5.1): route -> permute -> fc1 -> experts (up, relu^2,
+ * down) -> gate-weighted combine -> fc2 + shared expert.
+ *   x   device [T,H] bf16;  out device [T,H] bf16 (fp32 accumulation, one rounding)
+ *   ws  device workspace, >= moe_workspace_bytes(dims) bytes, 256-byte aligned;
+ *       it keeps the intermediates listed in moe_ws_layout.
+ * Intermediate roundings to bf16: z, h, y, y_lat, hs (the tensors the layer
+ * stores in bf16); every sum is fp32. */
+size_t moe_workspace_bytes(const moe_dims* dims);
+int moe_workspace_layout(const moe_dims* dims, moe_ws_layout* layout);
+int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* Library ABI version (major*100 + minor). */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_API_H */

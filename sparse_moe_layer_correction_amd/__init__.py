@@ -1,0 +1,312 @@
+"""MI355X-native LatentMoE layer forward.
+
+A thin Python binding over the C ABI of ``libmoe_mi355x.so`` (declared in
+``include/moe_api.h``). Every step of the layer runs in the library's HIP
+kernels; this module only checks tensor shapes and types, allocates outputs
+and workspaces with torch (device memory and streams are all torch is used
+for) and passes raw pointers. There is no fallback: if the library is missing
+or no GPU is present, the calls raise.
+
+The layer ("Nemotron 3 Ultra 架构 QA", CH5 Q5.1-Q5.8; the Nemotron-3 Ultra
+architecture walkthrough, section "LatentMoE 层"): sigmoid router over the
+uncompressed input with a bias-adjusted top-K choice and renormalised gates
+scaled by routed_scaling, an H->L latent projection, K non-gated relu^2
+experts L->I->L, a gate-weighted sum, the L->H projection, and a shared relu^2
+expert H->Is->H on the uncompressed input, added in parallel.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+__all__ = [
+    "MoEError", "MoEDims", "load_library", "library_path", "EXPORTS", "route", "permute", "forward",
+    "workspace_bytes", "route_workspace_bytes", "permute_workspace_bytes", "workspace_layout",
+    "LatentMoE",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libmoe_mi355x.so"
+
+# Every symbol include/moe_api.h declares.
+EXPORTS = (
+    "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
+    "moe_workspace_bytes", "moe_workspace_layout", "moe_forward", "moe_status_string", "moe_abi_version",
+)
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("K", ctypes.c_int32), ("Is", ctypes.c_int32),
+                ("routed_scaling", ctypes.c_float)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "corr_bias", "w_fc1", "w_up", "w_down", "w_fc2",
+                                              "w_sh_up", "w_sh_down")]
+
+
+_LAYOUT_FIELDS = ("idx", "gate", "gap", "offsets", "row_token", "slot_row", "z", "h", "y", "y_lat", "hs", "total")
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS]
+
+
+@dataclass(frozen=True)
+class MoEDims:
+    T: int
+    H: int
+    L: int
+    E: int
+    I: int
+    K: int
+    Is: int
+    routed_scaling: float = 5.0
+
+    def c(self) -> _Dims:
+        return _Dims(self.T, self.H, self.L, self.E, self.I, self.K, self.Is, self.routed_scaling)
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("MOE_MI355X_LIB", os.path.join(_PKG, LIB_NAME))
+
+
+def load_library(path: Optional[str] = None):
+    """Load the HIP library (built by ``python -m sparse_moe_layer_correction_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise MoEError(f"{p} not found: build it with `python -m sparse_moe_layer_correction_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    dims_p = ctypes.POINTER(_Dims)
+    sig = {
+        "moe_route_workspace_bytes": (sz, [dims_p]),
+        "moe_permute_workspace_bytes": (sz, [dims_p]),
+        "moe_workspace_bytes": (sz, [dims_p]),
+        "moe_workspace_layout": (i32, [dims_p, ctypes.POINTER(_Layout)]),
+        "moe_route": (i32, [dims_p, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_permute": (i32, [dims_p, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_forward": (i32, [dims_p, ctypes.POINTER(_Weights), vp, vp, vp, sz, vp]),
+        "moe_status_string": (ctypes.c_char_p, [i32]),
+        "moe_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise MoEError(f"moe call failed ({rc}): {load_library().moe_status_string(rc).decode()}")
+
+
+# ----------------------------------------------------------------------------
+# tensor plumbing
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on the GPU device {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _workspace(nbytes: int, device, ws=None):
+    torch = _torch()
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise MoEError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def route_workspace_bytes(dims: MoEDims) -> int:
+    d = dims.c()
+    return load_library().moe_route_workspace_bytes(ctypes.byref(d))
+
+
+def permute_workspace_bytes(dims: MoEDims) -> int:
+    d = dims.c()
+    return load_library().moe_permute_workspace_bytes(ctypes.byref(d))
+
+
+def workspace_bytes(dims: MoEDims) -> int:
+    d = dims.c()
+    return load_library().moe_workspace_bytes(ctypes.byref(d))
+
+
+def workspace_layout(dims: MoEDims) -> Dict[str, int]:
+    d = dims.c()
+    lay = _Layout()
+    _check(load_library().moe_workspace_layout(ctypes.byref(d), ctypes.byref(lay)))
+    return {n: getattr(lay, n) for n in _LAYOUT_FIELDS}
+
+
+# ----------------------------------------------------------------------------
+# the three calls of the C ABI
+# ----------------------------------------------------------------------------
+
+def route(x, w_router, corr_bias, K: int, routed_scaling: float = 5.0, *, with_gap: bool = True,
+          ws=None, stream=None):
+    """Router: returns (topk_idx [T,K] int32, topk_gate [T,K] fp32, gap [T] fp32 or None)."""
+    torch = _torch()
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, H), dev)
+    _need(w_router, "w_router", torch.float32, (E, H), dev)
+    _need(corr_bias, "corr_bias", torch.float32, (E,), dev)
+    dims = MoEDims(T, H, 64, E, 64, K, 64, routed_scaling)
+    d = dims.c()
+    lib = load_library()
+    idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+    gate = torch.empty(T, K, dtype=torch.float32, device=dev)
+    gap = torch.empty(T, dtype=torch.float32, device=dev) if with_gap else None
+    nbytes = lib.moe_route_workspace_bytes(ctypes.byref(d))
+    if nbytes == 0:
+        _check(lib.moe_route(ctypes.byref(d), None, None, None, None, None, None, None, 0, None))
+    w = _workspace(nbytes, dev, ws)
+    _check(lib.moe_route(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(corr_bias), _ptr(idx), _ptr(gate),
+                         _ptr(gap), _ptr(w), nbytes, _stream(stream)))
+    return idx, gate, gap
+
+
+def permute(topk_idx, E: int, src=None, *, ws=None, stream=None):
+    """Group the T*K slots by expert (tokens ascending within an expert).
+
+    Returns (expert_offsets [E+1], row_token [T*K], slot_row [T,K], dst [T*K,C] or None)."""
+    torch = _torch()
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    _need(topk_idx, "topk_idx", torch.int32, (T, K), dev)
+    C = 0
+    if src is not None:
+        C = src.shape[1]
+        _need(src, "src", torch.bfloat16, (T, C), dev)
+    dims = MoEDims(T, 64, 64, E, 64, K, 64)
+    d = dims.c()
+    lib = load_library()
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(T * K, dtype=torch.int32, device=dev)
+    slot_row = torch.empty(T, K, dtype=torch.int32, device=dev)
+    dst = torch.empty(T * K, C, dtype=torch.bfloat16, device=dev) if src is not None else None
+    nbytes = lib.moe_permute_workspace_bytes(ctypes.byref(d))
+    if nbytes == 0:
+        _check(lib.moe_permute(ctypes.byref(d), None, None, 0, None, None, None, None, None, 0, None))
+    w = _workspace(nbytes, dev, ws)
+    _check(lib.moe_permute(ctypes.byref(d), _ptr(topk_idx), _ptr(src), C, _ptr(dst), _ptr(offsets),
+                           _ptr(row_token), _ptr(slot_row), _ptr(w), nbytes, _stream(stream)))
+    return offsets, row_token, slot_row, dst
+
+
+_WEIGHT_SPECS = ("w_router", "corr_bias", "w_fc1", "w_up", "w_down", "w_fc2", "w_sh_up", "w_sh_down")
+
+
+def _weight_struct(dims: MoEDims, w: Dict, dev):
+    torch = _torch()
+    H, L, E, I, Is = dims.H, dims.L, dims.E, dims.I, dims.Is
+    shapes = {"w_router": ((E, H), torch.float32), "corr_bias": ((E,), torch.float32),
+              "w_fc1": ((L, H), torch.bfloat16), "w_up": ((E, I, L), torch.bfloat16),
+              "w_down": ((E, L, I), torch.bfloat16), "w_fc2": ((H, L), torch.bfloat16),
+              "w_sh_up": ((Is, H), torch.bfloat16), "w_sh_down": ((H, Is), torch.bfloat16)}
+    for n in _WEIGHT_SPECS:
+        shp, dt = shapes[n]
+        _need(w[n], n, dt, shp, dev)
+    return _Weights(*[_ptr(w[n]) for n in _WEIGHT_SPECS])
+
+
+def dims_from(x, weights: Dict, K: int, routed_scaling: float = 5.0) -> MoEDims:
+    T, H = x.shape
+    E, I, L = weights["w_up"].shape
+    Is = weights["w_sh_up"].shape[0]
+    return MoEDims(T, H, L, E, I, K, Is, routed_scaling)
+
+
+def forward(x, weights: Dict, K: int, routed_scaling: float = 5.0, *, out=None, ws=None, stream=None):
+    """Whole layer forward; returns out [T,H] bf16. ``ws`` (uint8, >= workspace_bytes) keeps
+    the intermediates at the offsets of ``workspace_layout``."""
+    torch = _torch()
+    dims = dims_from(x, weights, K, routed_scaling)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (dims.T, dims.H), dev)
+    wstruct = _weight_struct(dims, weights, dev)
+    d = dims.c()
+    lib = load_library()
+    if out is None:
+        out = torch.empty(dims.T, dims.H, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (dims.T, dims.H), dev)
+    nbytes = lib.moe_workspace_bytes(ctypes.byref(d))
+    if nbytes == 0:
+        _check(lib.moe_forward(ctypes.byref(d), ctypes.byref(wstruct), None, None, None, 0, None))
+    w = _workspace(nbytes, dev, ws)
+    _check(lib.moe_forward(ctypes.byref(d), ctypes.byref(wstruct), _ptr(x), _ptr(out), _ptr(w),
+                           w.numel() * w.element_size(), _stream(stream)))
+    return out
+
+
+class LatentMoE:
+    """The layer with its weights and a reusable workspace (no allocation per call)."""
+
+    def __init__(self, weights: Dict, K: int, routed_scaling: float = 5.0, max_tokens: int = 1):
+        self.weights = weights
+        self.K = K
+        self.routed_scaling = routed_scaling
+        self._ws = None
+        self._ws_tokens = 0
+        self.reserve(max_tokens)
+
+    def reserve(self, tokens: int):
+        torch = _torch()
+        w = self.weights
+        E, I, L = w["w_up"].shape
+        dims = MoEDims(tokens, w["w_fc1"].shape[1], L, E, I, self.K, w["w_sh_up"].shape[0], self.routed_scaling)
+        if tokens > self._ws_tokens:
+            self._ws = torch.empty(workspace_bytes(dims), dtype=torch.uint8, device=w["w_fc1"].device)
+            self._ws_tokens = tokens
+
+    def __call__(self, x, out=None, stream=None):
+        self.reserve(x.shape[0])
+        return forward(x, self.weights, self.K, self.routed_scaling, out=out, ws=self._ws, stream=stream)
+
+    @property
+    def workspace(self):
+        return self._ws

@@ -1,0 +1,30 @@
+// Instantiations and launcher of the bf16 MFMA GEMM (gemm.h).
+#include "kernels.h"
+
+namespace moe {
+
+TileShape tile_shape(int cfg) {
+  switch (cfg) {
+    case TILE_256x256: return {256, 256};
+    case TILE_128x128: return {128, 128};
+    case TILE_64x256: return {64, 256};
+    default: return {0, 0};
+  }
+}
+
+hipError_t launch_gemm(GemmLaunch& L, int cfg, hipStream_t st) {
+  int64_t total = 0;
+  for (int i = 0; i < L.np; ++i) total += (int64_t)L.p[i].mtiles * L.p[i].ntiles;
+  L.tiles0 = L.p[0].mtiles * L.p[0].ntiles;
+  if (total <= 0) return hipSuccess;
+  const dim3 grid((unsigned)total);
+  switch (cfg) {
+    case TILE_256x256: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4>), grid, dim3(512), 0, st, L); break;
+    case TILE_128x128: hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2>), grid, dim3(256), 0, st, L); break;
+    case TILE_64x256: hipLaunchKernelGGL((gemm_bf16_kernel<64, 256, 1, 4>), grid, dim3(256), 0, st, L); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

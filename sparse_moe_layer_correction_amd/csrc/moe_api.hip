@@ -1,0 +1,353 @@
+// C ABI of the LatentMoE layer forward: argument checks, workspace carving and
+// the launch sequence. Host code only; every step of the layer runs in the
+// kernels of router.hip, permute.hip, gemm.hip and combine.hip.
+#include "../../include/moe_api.h"
+
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Tile shape of the grouped expert products; the permutation lays out the
+// M-tile table for this BM.
+constexpr int kGroupedCfg = TILE_256x256;
+constexpr int kGroupedBM = 256;
+
+struct Layout {
+  // route
+  size_t wsplit, logits;
+  // permute
+  size_t masks, base, counts, tile_e, tile_m0, n_mtiles;
+  // forward
+  size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat;
+  size_t route_end, permute_begin, permute_end, total;
+  int64_t ldl;         // logits row stride (E rounded up to 64)
+  int nblk;            // token blocks of 64
+  int max_mtiles;      // M-tile table capacity
+};
+
+// Which fields of moe_dims a call reads.
+enum DimsUse { USE_ROUTE = 1, USE_PERMUTE = 2, USE_ALL = 3 };
+
+bool dims_ok(const moe_dims* d, int* status, int use = USE_ALL) {
+  *status = MOE_ERR_INVALID;
+  if (d == nullptr) return false;
+  if (d->T <= 0 || d->E <= 0 || d->K <= 0 || d->K > d->E) return false;
+  if ((use & USE_ROUTE) && d->H <= 0) return false;
+  if (use == USE_ALL && (d->L <= 0 || d->I <= 0 || d->Is <= 0)) return false;
+  *status = MOE_ERR_UNSUPPORTED;
+  if (d->E > kMaxExperts || d->K > kMaxTopK) return false;
+  if ((use & USE_ROUTE) && d->H % 64) return false;
+  if (use == USE_ALL && (d->L % 64 || d->I % 64 || d->Is % 64)) return false;
+  // permuted rows are indexed with int32; byte offsets of one tensor stay below 2^40
+  const int64_t tk = (int64_t)d->T * d->K;
+  if (tk > (int64_t)0x7FFFFFFF) return false;
+  *status = MOE_OK;
+  return true;
+}
+
+// moe_dims with the fields a partial call does not read zeroed, for the layout.
+moe_dims only_used(const moe_dims& d, int use) {
+  moe_dims u = d;
+  if (!(use & USE_ROUTE)) u.H = 0;
+  if (use != USE_ALL) { u.L = 0; u.I = 0; u.Is = 0; }
+  return u;
+}
+
+Layout make_layout(const moe_dims& d) {
+  Layout l{};
+  const int64_t T = d.T, H = d.H, L = d.L, E = d.E, I = d.I, K = d.K, Is = d.Is, TK = T * K;
+  l.ldl = (E + 63) / 64 * 64;
+  l.nblk = (int)((T + 63) / 64);
+  l.max_mtiles = (int)(TK / kGroupedBM + E + 1);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  l.wsplit = take(3 * E * H * 2);
+  l.logits = take(T * l.ldl * 4);
+  l.route_end = o;
+  l.permute_begin = o;
+  l.masks = take(E * l.nblk * 8);
+  l.base = take(E * l.nblk * 4);
+  l.counts = take(E * 4);
+  l.tile_e = take((size_t)l.max_mtiles * 4);
+  l.tile_m0 = take((size_t)l.max_mtiles * 4);
+  l.n_mtiles = take(4);
+  l.permute_end = o;
+  l.idx = take(TK * 4);
+  l.gate = take(TK * 4);
+  l.gap = take(T * 4);
+  l.offsets = take((E + 1) * 4);
+  l.row_token = take(TK * 4);
+  l.slot_row = take(TK * 4);
+  l.z = take(T * L * 2);
+  l.hs = take(T * Is * 2);
+  l.h = take(TK * I * 2);
+  l.y = take(TK * L * 2);
+  l.y_lat = take(T * L * 2);
+  l.total = o;
+  return l;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(ws) + off); }
+
+bool ws_ok(const void* ws, size_t have, size_t need) {
+  return ws != nullptr && have >= need && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Dense problem: C[M, N] = epi(sum_s A_s . B_s^T).
+GemmProblem dense_problem(int cfg, int M, int N, int Nb, void* C, int64_t ldc, int epi) {
+  GemmProblem p{};
+  const TileShape ts = tile_shape(cfg);
+  p.M = M;
+  p.N = N;
+  p.Nb = Nb;
+  p.C = C;
+  p.ldc = ldc;
+  p.epi = epi;
+  p.mtiles = (M + ts.BM - 1) / ts.BM;
+  p.ntiles = (N + ts.BN - 1) / ts.BN;
+  p.group_m = 4;
+  return p;
+}
+
+void add_seg(GemmProblem& p, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int K) {
+  p.seg[p.nseg++] = KSeg{A, B, lda, ldb, K};
+}
+
+int choose_dense_cfg(int M, int N) {
+  if (M >= 256 && N >= 256) return TILE_256x256;
+  if (M <= 64 && N >= 256) return TILE_64x256;
+  return TILE_128x128;
+}
+
+int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float* w_router, const float* bias,
+              int32_t* idx, float* gate, float* gap, void* ws, hipStream_t st) {
+  uint16_t* parts = at<uint16_t>(ws, l.wsplit);
+  float* logits = at<float>(ws, l.logits);
+  hipError_t e = launch_split_router_weight(w_router, d.E, d.H, parts, st);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int cfg = choose_dense_cfg(d.T, (int)l.ldl);
+  GemmLaunch L{};
+  L.np = 1;
+  L.p[0] = dense_problem(cfg, d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32);
+  const int64_t EH = (int64_t)d.E * d.H;
+  for (int s = 0; s < 3; ++s) add_seg(L.p[0], x, d.H, parts + s * EH, d.H, d.H);
+  e = launch_gemm(L, cfg, st);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_topk(logits, l.ldl, bias, d.T, d.E, d.K, d.routed_scaling, idx, gate, gap, st);
+  return hip_status(e);
+}
+
+// The permute scratch of a workspace whose first byte sits at layout offset `origin`.
+PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
+  return PermuteScratch{at<uint64_t>(ws, l.masks - origin), at<int32_t>(ws, l.base - origin),
+                        at<int32_t>(ws, l.counts - origin), at<int32_t>(ws, l.tile_e - origin),
+                        at<int32_t>(ws, l.tile_m0 - origin), at<int32_t>(ws, l.n_mtiles - origin)};
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return 100; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument (null pointer, non-positive size, K > E or bad row length)";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported size (H, L, I, Is must be multiples of 64; E <= 1024; K <= 64; T*K < 2^31)";
+    case MOE_ERR_WORKSPACE: return "workspace null, too small or not 256-byte aligned";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_route_workspace_bytes(const moe_dims* dims) {
+  int st;
+  if (!dims_ok(dims, &st, USE_ROUTE)) return 0;
+  return make_layout(only_used(*dims, USE_ROUTE)).route_end;
+}
+
+size_t moe_permute_workspace_bytes(const moe_dims* dims) {
+  int st;
+  if (!dims_ok(dims, &st, USE_PERMUTE)) return 0;
+  const Layout l = make_layout(only_used(*dims, USE_PERMUTE));
+  return l.permute_end - l.permute_begin;
+}
+
+size_t moe_workspace_bytes(const moe_dims* dims) {
+  int st;
+  if (!dims_ok(dims, &st)) return 0;
+  return make_layout(*dims).total;
+}
+
+int moe_workspace_layout(const moe_dims* dims, moe_ws_layout* out) {
+  int st;
+  if (!dims_ok(dims, &st)) return st;
+  if (out == nullptr) return MOE_ERR_INVALID;
+  const Layout l = make_layout(*dims);
+  out->idx = l.idx;
+  out->gate = l.gate;
+  out->gap = l.gap;
+  out->offsets = l.offsets;
+  out->row_token = l.row_token;
+  out->slot_row = l.slot_row;
+  out->z = l.z;
+  out->h = l.h;
+  out->y = l.y;
+  out->y_lat = l.y_lat;
+  out->hs = l.hs;
+  out->total = l.total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_dims* dims, const uint16_t* x, const float* w_router, const float* corr_bias,
+              int32_t* topk_idx, float* topk_gate, float* topk_gap, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  int st;
+  if (!dims_ok(dims, &st, USE_ROUTE)) return st;
+  if (!x || !w_router || !corr_bias || !topk_idx || !topk_gate) return MOE_ERR_INVALID;
+  const Layout l = make_layout(only_used(*dims, USE_ROUTE));
+  if (!ws_ok(ws, ws_bytes, l.route_end)) return MOE_ERR_WORKSPACE;
+  return run_route(*dims, l, x, w_router, corr_bias, topk_idx, topk_gate, topk_gap, ws, stream);
+}
+
+int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* src, int32_t C, uint16_t* dst,
+                int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  int st;
+  if (!dims_ok(dims, &st, USE_PERMUTE)) return st;
+  if (!topk_idx || !expert_offsets || !row_token || !slot_row) return MOE_ERR_INVALID;
+  if ((src == nullptr) != (dst == nullptr)) return MOE_ERR_INVALID;
+  if (src != nullptr && (C <= 0 || C % 8 != 0)) return MOE_ERR_INVALID;
+  const Layout l = make_layout(only_used(*dims, USE_PERMUTE));
+  const size_t need = l.permute_end - l.permute_begin;
+  if (!ws_ok(ws, ws_bytes, need)) return MOE_ERR_WORKSPACE;
+  // the caller's workspace holds only the permute scratch
+  hipError_t e = launch_permute_maps(topk_idx, dims->T, dims->K, dims->E, kGroupedBM,
+                                     permute_scratch(l, ws, l.permute_begin),
+                                     expert_offsets, row_token, slot_row, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (src != nullptr) e = launch_gather_rows(src, C, row_token, (int64_t)dims->T * dims->K, dst, stream);
+  return hip_status(e);
+}
+
+int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  int st;
+  if (!dims_ok(dims, &st)) return st;
+  if (!w || !x || !out || !w->w_router || !w->corr_bias || !w->w_fc1 || !w->w_up || !w->w_down || !w->w_fc2 ||
+      !w->w_sh_up || !w->w_sh_down)
+    return MOE_ERR_INVALID;
+  const moe_dims& d = *dims;
+  const Layout l = make_layout(d);
+  if (!ws_ok(ws, ws_bytes, l.total)) return MOE_ERR_WORKSPACE;
+  const int64_t T = d.T, H = d.H, L = d.L, I = d.I, Is = d.Is, TK = T * d.K;
+
+  int32_t* idx = at<int32_t>(ws, l.idx);
+  float* gate = at<float>(ws, l.gate);
+  int32_t* offsets = at<int32_t>(ws, l.offsets);
+  int32_t* row_token = at<int32_t>(ws, l.row_token);
+  int32_t* slot_row = at<int32_t>(ws, l.slot_row);
+  uint16_t* z = at<uint16_t>(ws, l.z);
+  uint16_t* hs = at<uint16_t>(ws, l.hs);
+  uint16_t* h = at<uint16_t>(ws, l.h);
+  uint16_t* y = at<uint16_t>(ws, l.y);
+  uint16_t* y_lat = at<uint16_t>(ws, l.y_lat);
+
+  // 1. router
+  int rc = run_route(d, l, x, w->w_router, w->corr_bias, idx, gate, at<float>(ws, l.gap), ws, stream);
+  if (rc != MOE_OK) return rc;
+
+  // 2. permutation maps and the M-tile table of the grouped products
+  const PermuteScratch ps = permute_scratch(l, ws, 0);
+  if (launch_permute_maps(idx, d.T, d.K, d.E, kGroupedBM, ps, offsets, row_token, slot_row, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+
+  // 3. x read by one launch for fc1 (z) and the shared expert's up + relu^2 (hs)
+  {
+    const int cfg = choose_dense_cfg(d.T, std::min(d.L, d.Is));
+    GemmLaunch G{};
+    G.np = 2;
+    G.p[0] = dense_problem(cfg, d.T, d.L, d.L, z, L, EPI_BF16);
+    add_seg(G.p[0], x, H, w->w_fc1, H, d.H);
+    G.p[1] = dense_problem(cfg, d.T, d.Is, d.Is, hs, Is, EPI_RELU2_BF16);
+    add_seg(G.p[1], x, H, w->w_sh_up, H, d.H);
+    if (launch_gemm(G, cfg, stream) != hipSuccess) return MOE_ERR_HIP;
+  }
+
+  // 4. expert up + relu^2 over the permuted rows; z rows gathered on load
+  {
+    const TileShape ts = tile_shape(kGroupedCfg);
+    GemmLaunch G{};
+    G.np = 1;
+    GemmProblem& p = G.p[0];
+    p.N = d.I;
+    p.Nb = d.I;
+    p.gather = row_token;
+    p.tile_e = ps.tile_e;
+    p.tile_m0 = ps.tile_m0;
+    p.n_mtiles = ps.n_mtiles;
+    p.offsets = offsets;
+    p.b_estride = I * L;
+    p.C = h;
+    p.ldc = I;
+    p.epi = EPI_RELU2_BF16;
+    p.mtiles = l.max_mtiles;
+    p.ntiles = (d.I + ts.BN - 1) / ts.BN;
+    p.group_m = 4;
+    add_seg(p, z, L, w->w_up, L, d.L);
+    if (launch_gemm(G, kGroupedCfg, stream) != hipSuccess) return MOE_ERR_HIP;
+  }
+
+  // 5. expert down over the permuted rows
+  {
+    const TileShape ts = tile_shape(kGroupedCfg);
+    GemmLaunch G{};
+    G.np = 1;
+    GemmProblem& p = G.p[0];
+    p.N = d.L;
+    p.Nb = d.L;
+    p.tile_e = ps.tile_e;
+    p.tile_m0 = ps.tile_m0;
+    p.n_mtiles = ps.n_mtiles;
+    p.offsets = offsets;
+    p.b_estride = L * I;
+    p.C = y;
+    p.ldc = L;
+    p.epi = EPI_BF16;
+    p.mtiles = l.max_mtiles;
+    p.ntiles = (d.L + ts.BN - 1) / ts.BN;
+    p.group_m = 4;
+    add_seg(p, h, I, w->w_down, I, d.I);
+    if (launch_gemm(G, kGroupedCfg, stream) != hipSuccess) return MOE_ERR_HIP;
+  }
+
+  // 6. gate-weighted combine in the latent
+  if (launch_combine(y, gate, slot_row, d.T, d.K, d.L, y_lat, stream) != hipSuccess) return MOE_ERR_HIP;
+
+  // 7. out = y_lat . W_fc2^T + hs . W_sd^T, one fp32 accumulator, one rounding
+  {
+    const int cfg = choose_dense_cfg(d.T, d.H);
+    GemmLaunch G{};
+    G.np = 1;
+    G.p[0] = dense_problem(cfg, d.T, d.H, d.H, out, H, EPI_BF16);
+    add_seg(G.p[0], y_lat, L, w->w_fc2, L, d.L);
+    add_seg(G.p[0], hs, Is, w->w_sh_down, Is, d.Is);
+    if (launch_gemm(G, cfg, stream) != hipSuccess) return MOE_ERR_HIP;
+  }
+  (void)TK;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,252 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle, on an MI355X.
+
+Bars: routing indices bit-exact except on near-tie tokens (oracle gap < 1e-4,
+counted; the GPU's choice must then lie inside the tie band), gates within the
+derived fp32 tolerance, the permutation bit-exact, the layer output within
+max|err| / max|ref| <= 2e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_layer_correction_amd as M
+import workloads as W
+from gpu_util import (OUT_TOL, bf16_dev_to_f64, check_routing, device_inputs, host_f32, log,
+                      oracle_forward_tokens, oracle_route, relerr, u16, weights_of)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    M.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_route(d):
+    cfg = d["cfg"]
+    log(f"[route] {cfg.name} T={cfg.T} E={cfg.E} K={cfg.K}")
+    idx, gate, gap = M.route(d["x"], d["w_router"], d["corr_bias"], cfg.K, cfg.routed_scaling)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), gate.cpu().numpy(), gap.cpu().numpy()
+
+
+def run_forward(d):
+    cfg = d["cfg"]
+    dims = M.dims_from(d["x"], weights_of(d), cfg.K, cfg.routed_scaling)
+    ws = torch.empty(M.workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    log(f"[forward] {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} K={cfg.K} ws={ws.numel() / 2**30:.2f} GiB")
+    out = M.forward(d["x"], weights_of(d), cfg.K, cfg.routed_scaling, ws=ws)
+    torch.cuda.synchronize()
+    return out, ws, M.workspace_layout(dims)
+
+
+def ws_view(ws, lay, name, dtype, shape):
+    n = int(np.prod(shape))
+    es = torch.tensor([], dtype=dtype).element_size()
+    return ws[lay[name]:lay[name] + n * es].view(dtype).view(*shape)
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}),
+    ("tiny", dict(T=37)),                    # ragged token count
+    ("tiny", dict(K=16)),                    # K == E: every expert, gap = +inf
+    ("tiny", dict(K=1)),
+    ("nano", dict(T=1024)),
+    ("super", dict(T=2048)),
+    ("ultra_decode1", {}),
+    ("ultra_decode64", {}),
+    ("ultra_prefill", {}),
+])
+def test_route_parity(name, over):
+    d = device_inputs(name, **over)
+    idx, gate, gap = run_route(d)
+    ref = oracle_route(d)
+    flagged = check_routing(idx, gate, gap, ref, label=f"{name}{over}")
+    log(f"[route] {name}{over}: {flagged} of {d['cfg'].T} tokens in the tie band")
+
+
+def test_route_forced_bias():
+    """A +2 bias on a chosen set forces that set for every token (sigmoid < 1)."""
+    d = dict(device_inputs("tiny"))
+    forced = [2, 3, 7, 11]
+    b = torch.zeros_like(d["corr_bias"])
+    b[forced] = 2.0
+    d["corr_bias"] = b
+    idx, gate, _ = run_route(d)
+    assert np.array_equal(idx, np.tile(forced, (d["cfg"].T, 1)))
+    ref = oracle_route(d)
+    assert np.max(np.abs(gate - ref.gate) / ref.gate) < 1e-5
+
+
+def test_route_ties_go_to_lower_index():
+    d = dict(device_inputs("tiny"))
+    wr = d["w_router"].clone()
+    wr[11] = wr[3]
+    b = torch.zeros_like(d["corr_bias"])
+    b[[0, 1, 2]] = 2.0
+    b[[3, 11]] = 1.0
+    d["w_router"], d["corr_bias"] = wr, b
+    idx, _, gap = run_route(d)
+    assert np.array_equal(idx, np.tile([0, 1, 2, 3], (d["cfg"].T, 1)))
+    assert np.all(gap == 0.0)
+
+
+# ----------------------------------------------------------------------------
+# permutation
+# ----------------------------------------------------------------------------
+
+def _check_perm(idx, E, src=None):
+    tidx = torch.from_numpy(idx.astype(np.int32)).cuda()
+    tsrc = None if src is None else src
+    log(f"[permute] T={idx.shape[0]} K={idx.shape[1]} E={E}")
+    off, rt, sr, dst = M.permute(tidx, E, tsrc)
+    torch.cuda.synchronize()
+    ref = oracle.permute(idx, E)
+    assert np.array_equal(off.cpu().numpy(), ref.offsets)
+    assert np.array_equal(rt.cpu().numpy(), ref.row_token)
+    assert np.array_equal(sr.cpu().numpy(), ref.slot_row)
+    if src is not None:
+        assert torch.equal(dst, src[rt.long()])
+
+
+@pytest.mark.parametrize("T,E,K,seed", [(64, 16, 4, 0), (37, 16, 4, 1), (1, 512, 22, 2), (1000, 128, 8, 3),
+                                        (4097, 40, 40, 4), (130, 1024, 64, 5), (16384, 512, 22, 6)])
+def test_permute_random(T, E, K, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K]
+    idx = np.sort(idx, axis=1)
+    src = torch.randn(T, 72, device="cuda").to(torch.bfloat16)
+    _check_perm(idx, E, src)
+
+
+def test_permute_skewed_with_idle_experts():
+    T, E, K = 3000, 64, 6
+    idx = np.stack([np.sort(np.array([0, 1, 2, 3, 4, 5 + (t % 3)])[:K]) for t in range(T)])
+    _check_perm(idx, E)
+
+
+def test_permute_router_output_ultra():
+    d = device_inputs("ultra_prefill")
+    idx, _, _ = run_route(d)
+    _check_perm(idx, d["cfg"].E, src=None)
+
+
+# ----------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------
+
+def _compare_tokens(d, out, ws, lay, tokens, idx_gpu, label):
+    cfg = d["cfg"]
+    ref_r = oracle_route(d, tokens)
+    flagged = ref_r.gap < oracle.GAP_FLAG
+    override = ref_r.idx.copy()
+    override[flagged] = idx_gpu[tokens][flagged]     # follow the GPU on near-ties
+    log(f"[oracle] {label}: {len(tokens)} tokens ({int(flagged.sum())} in the tie band)")
+    ref = oracle_forward_tokens(d, tokens, idx_override=override, keep=True)
+    got = bf16_dev_to_f64(out[torch.as_tensor(tokens, device="cuda")])
+    e_out = relerr(got, ref["out"])
+    z = bf16_dev_to_f64(ws_view(ws, lay, "z", torch.bfloat16, (cfg.T, cfg.L))[torch.as_tensor(tokens, device="cuda")])
+    hs = bf16_dev_to_f64(ws_view(ws, lay, "hs", torch.bfloat16, (cfg.T, cfg.Is))[torch.as_tensor(tokens, device="cuda")])
+    yl = bf16_dev_to_f64(ws_view(ws, lay, "y_lat", torch.bfloat16, (cfg.T, cfg.L))[torch.as_tensor(tokens, device="cuda")])
+    e_z, e_hs, e_yl = relerr(z, ref["z"]), relerr(hs, ref["hs"]), relerr(yl, ref["y_lat"])
+    log(f"[parity] {label}: out {e_out:.2e}  z {e_z:.2e}  hs {e_hs:.2e}  y_lat {e_yl:.2e}")
+    assert e_z < OUT_TOL and e_hs < OUT_TOL and e_yl < OUT_TOL
+    assert e_out < OUT_TOL, f"{label}: max|err|/max|ref| = {e_out:.3g}"
+    return e_out
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", dict(T=37)), ("tiny", dict(T=1)),
+                                       ("tiny", dict(K=16)), ("tiny", dict(K=1))])
+def test_forward_tiny_full(name, over):
+    d = device_inputs(name, **over)
+    cfg = d["cfg"]
+    out, ws, lay = run_forward(d)
+    idx = ws_view(ws, lay, "idx", torch.int32, (cfg.T, cfg.K)).cpu().numpy()
+    tokens = np.arange(cfg.T)
+    _compare_tokens(d, out, ws, lay, tokens, idx, f"{name}{over}")
+    # the expert intermediates too, row by row in the permuted order
+    ref = oracle_forward_tokens(d, tokens, keep=True)
+    if np.array_equal(ref["idx"], idx):
+        TK = cfg.T * cfg.K
+        h = bf16_dev_to_f64(ws_view(ws, lay, "h", torch.bfloat16, (TK, cfg.I)))
+        y = bf16_dev_to_f64(ws_view(ws, lay, "y", torch.bfloat16, (TK, cfg.L)))
+        assert np.array_equal(ws_view(ws, lay, "row_token", torch.int32, (TK,)).cpu().numpy(), ref["row_token"])
+        assert relerr(h, ref["h"]) < OUT_TOL
+        assert relerr(y, ref["y"]) < OUT_TOL
+
+
+def _sample(T, n, seed):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    s.update({0, T - 1})
+    return np.array(sorted(s))
+
+
+@pytest.mark.parametrize("name,over,n", [
+    ("nano", dict(T=1024), 6),
+    ("super", dict(T=2048), 6),
+    ("ultra_decode1", {}, 1),
+    ("ultra_decode64", {}, 3),
+    ("ultra_prefill", {}, 3),
+])
+def test_forward_sampled(name, over, n):
+    d = device_inputs(name, **over)
+    cfg = d["cfg"]
+    out, ws, lay = run_forward(d)
+    idx = ws_view(ws, lay, "idx", torch.int32, (cfg.T, cfg.K)).cpu().numpy()
+    gate = ws_view(ws, lay, "gate", torch.float32, (cfg.T, cfg.K)).cpu().numpy()
+    gap = ws_view(ws, lay, "gap", torch.float32, (cfg.T,)).cpu().numpy()
+    # routing of every token
+    check_routing(idx, gate, gap, oracle_route(d), label=name)
+    # permutation maps of the forward equal the oracle's on the GPU's routing
+    p = oracle.permute(idx, cfg.E)
+    assert np.array_equal(ws_view(ws, lay, "offsets", torch.int32, (cfg.E + 1,)).cpu().numpy(), p.offsets)
+    assert np.array_equal(ws_view(ws, lay, "row_token", torch.int32, (cfg.T * cfg.K,)).cpu().numpy(), p.row_token)
+    # outputs on sampled tokens (tokens are independent)
+    _compare_tokens(d, out, ws, lay, _sample(cfg.T, n, 11), idx, f"{name}{over}")
+
+
+def test_forward_deterministic():
+    d = device_inputs("nano", T=512)
+    a, _, _ = run_forward(d)
+    b, _, _ = run_forward(d)
+    assert torch.equal(a, b)
+
+
+def test_zero_routed_path_leaves_shared_output():
+    """W_fc2 = 0: out must equal the shared expert alone (oracle on all tokens)."""
+    d = dict(device_inputs("tiny"))
+    d["w_fc2"] = torch.zeros_like(d["w_fc2"])
+    out, _, _ = run_forward(d)
+    ref = oracle_forward_tokens(d, np.arange(d["cfg"].T))
+    assert relerr(bf16_dev_to_f64(out), ref["out"]) < OUT_TOL
+
+
+def test_identity_experts():
+    """Identity experts on binary inputs give out[:, :L] = 5 x[:, :L] exactly."""
+    T, H, L, E, I, K, Is = 96, 128, 64, 8, 128, 3, 64
+    cfg = W.MoEConfig("ident", T=T, H=H, L=L, E=E, I=I, K=K, Is=Is, bias_halfwidth=0.1, seed=9,
+                      weight_key="ident")
+    d = W.make_inputs(cfg, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    d["x"] = torch.randint(0, 2, (T, H), generator=g).to(torch.bfloat16).cuda()
+    eye = torch.eye(L, dtype=torch.bfloat16, device="cuda")
+    d["w_fc1"] = torch.zeros(L, H, dtype=torch.bfloat16, device="cuda"); d["w_fc1"][:, :L] = eye
+    d["w_up"] = torch.zeros(E, I, L, dtype=torch.bfloat16, device="cuda"); d["w_up"][:, :L, :] = eye
+    d["w_down"] = torch.zeros(E, L, I, dtype=torch.bfloat16, device="cuda"); d["w_down"][:, :, :L] = eye
+    d["w_fc2"] = torch.zeros(H, L, dtype=torch.bfloat16, device="cuda"); d["w_fc2"][:L, :] = eye
+    d["w_sh_up"] = torch.zeros(Is, H, dtype=torch.bfloat16, device="cuda")
+    d["w_sh_down"] = torch.zeros(H, Is, dtype=torch.bfloat16, device="cuda")
+    d["cfg"] = cfg
+    out, _, _ = run_forward(d)
+    assert torch.equal(out[:, :L], 5.0 * d["x"][:, :L])
+    assert torch.all(out[:, L:] == 0)

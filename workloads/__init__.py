@@ -37,7 +37,7 @@ import torch
 
 __all__ = [
     "MoEConfig", "CONFIGS", "get_config", "gen_normal_bf16", "gen_normal_f32",
-    "gen_uniform_f32", "make_inputs", "expert_weights", "zipf_offsets",
+    "gen_uniform_f32", "make_inputs", "make_x", "make_weights", "expert_weights", "zipf_offsets",
     "f32_to_bf16_bits", "bf16_tensor_to_u16_numpy",
 ]
 
@@ -235,26 +235,29 @@ def expert_weights(cfg: MoEConfig, e0: int, e1: int, device="cpu"):
     return up, down
 
 
-def make_inputs(cfg: MoEConfig, device="cpu", with_experts: bool = True) -> Dict[str, torch.Tensor]:
-    """All inputs of one forward: x, router weight, bias and the seven weight tensors.
+def make_x(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    """The input rows x [T,H] bf16. Row t does not depend on T (a longer batch
+    extends a shorter one)."""
+    x = gen_normal_bf16(_wseed(cfg) * 7919 + cfg.x_tag, TAG_X, (cfg.T, cfg.H), 1.0, device)
+    if cfg.skew == "zipf1.1":
+        x[:, 0] = 1.0      # carries the per-expert logit offsets, see make_weights
+    return x
 
-    bf16 tensors are torch.bfloat16, fp32 ones torch.float32, all on ``device``.
-    """
+
+def make_weights(cfg: MoEConfig, device="cpu", with_experts: bool = True) -> Dict[str, torch.Tensor]:
+    """Router weight, bias and the weight tensors of the layer."""
     ws = _wseed(cfg)
-    T, H, L, E, I, Is = cfg.T, cfg.H, cfg.L, cfg.E, cfg.I, cfg.Is
+    H, L, E, I, Is = cfg.H, cfg.L, cfg.E, cfg.I, cfg.Is
     d: Dict[str, torch.Tensor] = {}
-    x = gen_normal_bf16(ws * 7919 + cfg.x_tag, TAG_X, (T, H), 1.0, device)
     wr = gen_normal_f32(ws, TAG_WR, (E, H), 1.0 / math.sqrt(H), device)
     if cfg.skew == "zipf1.1":
         # the offsets enter through the router product itself: x[:,0] = 1 and
         # w_router[:,0] = delta_e gives logit_e = delta_e + (the rest)
-        x[:, 0] = 1.0
         wr[:, 0] = torch.from_numpy(zipf_offsets(E, ws)).to(device)
     if cfg.bias_halfwidth > 0:
         bias = gen_uniform_f32(ws, TAG_BIAS, (E,), cfg.bias_halfwidth, device)
     else:
         bias = torch.zeros(E, dtype=torch.float32, device=device)
-    d["x"] = x
     d["w_router"] = wr
     d["corr_bias"] = bias
     d["w_fc1"] = gen_normal_bf16(ws, TAG_FC1, (L, H), 1.0 / math.sqrt(H), device)
@@ -265,6 +268,16 @@ def make_inputs(cfg: MoEConfig, device="cpu", with_experts: bool = True) -> Dict
         up, down = expert_weights(cfg, 0, E, device)
         d["w_up"] = up
         d["w_down"] = down
+    return d
+
+
+def make_inputs(cfg: MoEConfig, device="cpu", with_experts: bool = True) -> Dict[str, torch.Tensor]:
+    """All inputs of one forward: x, router weight, bias and the seven weight tensors.
+
+    bf16 tensors are torch.bfloat16, fp32 ones torch.float32, all on ``device``.
+    """
+    d = make_weights(cfg, device, with_experts)
+    d["x"] = make_x(cfg, device)
     return d
 
 
