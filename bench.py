@@ -1,0 +1,200 @@
+"""Benchmark of the LatentMoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ultra_prefill]
+
+A step is one whole forward (router, permutation, fc1 + shared up, expert up,
+expert down, combine, fc2 + shared down) over one batch of seeded synthetic
+input already resident in HBM. Prints one JSON line with the whole-layer
+throughput, the roofline of the dominant kernel (timed live with HIP events
+recorded on the forward's stream) and the CPU oracle timed on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "LatentMoE fwd tokens/s + TFLOP/s (Ultra shape); % MFMA peak / % HBM BW"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ("gemm.h", "common.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_moe_layer_correction_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def phase_work(cfg, n_touched: int):
+    """Algorithmic FLOPs and compulsory HBM bytes of each phase of one forward."""
+    T, H, L, E, I, K, Is = cfg.T, cfg.H, cfg.L, cfg.E, cfg.I, cfg.K, cfg.Is
+    TK = T * K
+    flops = dict(router_gemm=2 * T * H * E, fc1_shared_up=2 * T * H * (L + Is), expert_up=2 * TK * L * I,
+                 expert_down=2 * TK * I * L, fc2_shared_down=2 * T * (L + Is) * H)
+    bytes_ = dict(router_gemm=4 * E * H + 2 * T * H,
+                  fc1_shared_up=2 * H * (L + Is) + 2 * T * H + 2 * T * (L + Is),
+                  expert_up=2 * n_touched * I * L + 2 * T * L + 2 * TK * I,
+                  expert_down=2 * n_touched * L * I + 2 * TK * I + 2 * TK * L,
+                  fc2_shared_down=2 * H * (L + Is) + 2 * T * (L + Is) + 2 * T * H)
+    return flops, bytes_
+
+
+def cpu_baseline(d, cfg, idx_gpu, n_tokens: int):
+    """The oracle, as it stands, on n_tokens tokens of the same batch (host cores)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or 1
+    except Exception:
+        threads = 1
+    rng = np.random.default_rng(1234)
+    tokens = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
+    u = W.bf16_tensor_to_u16_numpy
+    # host copies of the inputs, untimed
+    need = sorted(set(idx_gpu[tokens].reshape(-1).tolist()))
+    experts = {e: (u(d["w_up"][e]), u(d["w_down"][e])) for e in need}
+
+    def expert(e):
+        if e not in experts:
+            experts[e] = (u(d["w_up"][e]), u(d["w_down"][e]))
+        return experts[e]
+
+    args = (u(d["x"][tokens]), d["w_router"].cpu().numpy(), d["corr_bias"].cpu().numpy(), u(d["w_fc1"]),
+            u(d["w_fc2"]), u(d["w_sh_up"]), u(d["w_sh_down"]))
+    t0 = time.perf_counter()
+    oracle.forward(*args, expert, cfg.K, cfg.routed_scaling, mirror=True)
+    dt = time.perf_counter() - t0
+    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(tokens)} of the {cfg.T} tokens of the {cfg.name} batch (tokens are independent), "
+                      f"whole layer per token in float64 with bf16 rounding; {dt:.1f} s on "
+                      f"{os.cpu_count()} host cores, BLAS threads {threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ultra_prefill",
+                    choices=["ultra_prefill", "ultra_decode64", "ultra_decode1", "nano", "super", "tiny"])
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the layer forward runs on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_layer_correction_amd as M
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = W.get_config(args.workload)
+    d = W.make_inputs(cfg, device="cuda")
+    weights = {k: v for k, v in d.items() if k != "x"}
+    dims = M.dims_from(d["x"], weights, cfg.K, cfg.routed_scaling)
+    ws = torch.empty(M.workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
+    lay = M.workspace_layout(dims)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        M.forward(d["x"], weights, cfg.K, cfg.routed_scaling, out=out, ws=ws)
+    torch.cuda.synchronize()
+
+    evs = [M.PhaseEvents() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        M.forward_profiled(d["x"], weights, cfg.K, cfg.routed_scaling, evs[i], out=out, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    per = [e.phase_ms() for e in evs]
+    phase_ms = {k: float(np.mean([p[k] for p in per])) for k in M.PHASES}
+    ev_ms = float(np.mean([sum(p.values()) for p in per]))
+
+    offsets = ws[lay["offsets"]:lay["offsets"] + 4 * (cfg.E + 1)].view(torch.int32).cpu().numpy()
+    n_touched = int(np.count_nonzero(np.diff(offsets)))
+    idx_gpu = ws[lay["idx"]:lay["idx"] + 4 * cfg.T * cfg.K].view(torch.int32).view(cfg.T, cfg.K).cpu().numpy()
+    flops, bytes_ = phase_work(cfg, n_touched)
+    total_flops = sum(flops.values())
+    tokens_per_s = cfg.T / (ms_per_step / 1e3)
+    tflops = total_flops / (ms_per_step / 1e3) / 1e12
+
+    prefill = cfg.T * cfg.K >= 4 * cfg.E * 64
+    gemm_phases = ["router_gemm", "fc1_shared_up", "expert_up", "expert_down", "fc2_shared_down"]
+    dom = max(gemm_phases, key=lambda k: phase_ms[k])
+    dur_s = phase_ms[dom] / 1e3
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        rec = tr.get(cfg.name, {}).get(dom)
+        if rec and rec.get("kernel_hash") == kernel_source_hash():
+            traffic = rec["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    if prefill:
+        achieved = flops[dom] / dur_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom,
+                    "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(phase_ms[dom], 4)}
+    else:
+        achieved = bytes_[dom] / dur_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
+                    "algorithmic_bytes_per_launch": bytes_[dom], "avg_launch_ms": round(phase_ms[dom], 4)}
+
+    layer_bytes = 4 * cfg.E * cfg.H + 2 * 2 * cfg.H * cfg.L + 2 * 2 * cfg.H * cfg.Is + \
+        n_touched * 2 * 2 * cfg.I * cfg.L + 2 * 2 * cfg.T * cfg.H
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; random weights of the stated shapes)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "L": cfg.L, "E": cfg.E, "I": cfg.I,
+                   "K": cfg.K, "Is": cfg.Is, "routed_scaling": cfg.routed_scaling},
+        "tflops": round(tflops, 2),
+        "mfma_frac_layer": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "hbm_gbs_layer": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "hbm_frac_layer": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        "experts_touched": n_touched,
+        "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "events_ms_per_step": round(ev_ms, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, cfg, idx_gpu, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -140,6 +140,27 @@ int moe_workspace_layout(const moe_dims* dims, moe_ws_layout* layout);
 int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Phases of moe_forward, in launch order. */
+enum moe_phase {
+  MOE_PHASE_ROUTER_SPLIT = 0,  /* fp32 router weight -> three bf16 parts */
+  MOE_PHASE_ROUTER_GEMM,       /* router logits */
+  MOE_PHASE_TOPK,              /* sigmoid, biased top-K, gates */
+  MOE_PHASE_PERMUTE,           /* masks, scans, scatter */
+  MOE_PHASE_FC1_SHARED_UP,     /* z = fc1(x) and hs = relu^2(sh_up(x)), one launch */
+  MOE_PHASE_EXPERT_UP,         /* h = relu^2(up_e(z)) over the permuted rows */
+  MOE_PHASE_EXPERT_DOWN,       /* y = down_e(h) */
+  MOE_PHASE_COMBINE,           /* y_lat = sum_k g_k y */
+  MOE_PHASE_FC2_SHARED_DOWN,   /* out = fc2(y_lat) + sh_down(hs), one launch */
+  MOE_N_PHASES
+};
+
+/* moe_forward with timing markers, for measurement: before phase i it records
+ * events[i] on `stream`, and after the last phase events[MOE_N_PHASES]
+ * (hipEventRecord; the caller creates and owns the events). n_events must be at
+ * least MOE_N_PHASES + 1, else MOE_ERR_INVALID. Same results as moe_forward. */
+int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out,
+                         void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events, int n_events);
+
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(int status);
 

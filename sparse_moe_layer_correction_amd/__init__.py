@@ -24,7 +24,7 @@ from typing import Dict, Optional
 __all__ = [
     "MoEError", "MoEDims", "load_library", "library_path", "EXPORTS", "route", "permute", "forward",
     "workspace_bytes", "route_workspace_bytes", "permute_workspace_bytes", "workspace_layout",
-    "LatentMoE",
+    "LatentMoE", "PhaseEvents", "forward_profiled", "PHASES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,8 +33,13 @@ LIB_NAME = "libmoe_mi355x.so"
 # Every symbol include/moe_api.h declares.
 EXPORTS = (
     "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
-    "moe_workspace_bytes", "moe_workspace_layout", "moe_forward", "moe_status_string", "moe_abi_version",
+    "moe_workspace_bytes", "moe_workspace_layout", "moe_forward", "moe_forward_profiled", "moe_status_string",
+    "moe_abi_version",
 )
+
+# enum moe_phase of include/moe_api.h
+PHASES = ("router_split", "router_gemm", "topk", "permute", "fc1_shared_up", "expert_up", "expert_down",
+          "combine", "fc2_shared_down")
 
 
 class MoEError(RuntimeError):
@@ -100,6 +105,8 @@ def load_library(path: Optional[str] = None):
         "moe_route": (i32, [dims_p, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_permute": (i32, [dims_p, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, sz, vp]),
         "moe_forward": (i32, [dims_p, ctypes.POINTER(_Weights), vp, vp, vp, sz, vp]),
+        "moe_forward_profiled": (i32, [dims_p, ctypes.POINTER(_Weights), vp, vp, vp, sz, vp,
+                                       ctypes.POINTER(ctypes.c_void_p), i32]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_abi_version": (i32, []),
     }
@@ -280,6 +287,56 @@ def forward(x, weights: Dict, K: int, routed_scaling: float = 5.0, *, out=None, 
     w = _workspace(nbytes, dev, ws)
     _check(lib.moe_forward(ctypes.byref(d), ctypes.byref(wstruct), _ptr(x), _ptr(out), _ptr(w),
                            w.numel() * w.element_size(), _stream(stream)))
+    return out
+
+
+class PhaseEvents:
+    """HIP events for moe_forward_profiled, created through the HIP runtime."""
+
+    def __init__(self, n: int = len(PHASES) + 1):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise MoEError("hipEventCreate failed")
+            self.events[i] = ev
+        self.n = n
+
+    def phase_ms(self):
+        """Duration of each phase of the last recorded forward (after a synchronize)."""
+        out = []
+        for i in range(self.n - 1):
+            ms = ctypes.c_float()
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.events[i], self.events[i + 1]) != 0:
+                raise MoEError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return dict(zip(PHASES, out))
+
+    def __del__(self):
+        try:
+            for i in range(self.n):
+                self._hip.hipEventDestroy(self.events[i])
+        except Exception:
+            pass
+
+
+def forward_profiled(x, weights: Dict, K: int, routed_scaling: float, events: "PhaseEvents", *, out, ws,
+                     stream=None):
+    """moe_forward_profiled: the forward with an event recorded before each phase."""
+    torch = _torch()
+    dims = dims_from(x, weights, K, routed_scaling)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (dims.T, dims.H), dev)
+    _need(out, "out", torch.bfloat16, (dims.T, dims.H), dev)
+    wstruct = _weight_struct(dims, weights, dev)
+    d = dims.c()
+    _check(load_library().moe_forward_profiled(ctypes.byref(d), ctypes.byref(wstruct), _ptr(x), _ptr(out),
+                                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
+                                               events.events, events.n))
     return out
 
 

@@ -10,12 +10,22 @@
 // out = y_lat.W_fc2^T + hs.W_sd^T is one product with K = L + Is, and the
 // router's three bf16 weight parts sum into one logit.
 //
-// Tiling: BM x BN x 64 per workgroup of 64*WM*WN threads (WM x WN wave
-// grid), v_mfma_f32_32x32x16_bf16 tiles, both operands staged through LDS
-// (double buffered, XOR-swizzled 16-byte chunks so MFMA fragment reads are
-// bank-conflict free), global loads for tile k+1 in flight while tile k is
-// multiplied. The MFMA takes the B fragment as its first operand so that each
-// lane ends up owning 4 consecutive output columns of one output row.
+// Data movement (gfx950):
+//  * global -> LDS with global_load_lds_dwordx4 (16 bytes per lane, no VGPR
+//    staging) into a ring of STAGES separate LDS arrays, one per stage, so the
+//    compiler's alias analysis can tell the stage being read from the stages
+//    being filled and does not wait for every DMA in flight;
+//  * one k tile is 32 bf16 deep (64 bytes per row = 4 chunks of 16 bytes);
+//    chunk c of row r sits in slot c ^ ((r >> 2) & 3): gfx950's LDS serves a
+//    ds_read_b128 16 lanes per cycle over 64 banks, and the 16 rows those lanes
+//    read then fall into the 16 distinct 16-byte slots of a 256-byte window;
+//  * the DMA of each lane is chosen so that the 64 lanes of a wave fill 1 KB
+//    of LDS contiguously in that swizzled order (rows stay fully coalesced);
+//  * every step waits for its own tile (vmcnt), passes one barrier and issues
+//    the tile STAGES-1 ahead into the stage freed by the previous step; past
+//    the end it re-reads the last tile, so the wait count never changes.
+// The MFMA is v_mfma_f32_32x32x16_bf16 with the B fragment as first operand,
+// so each lane owns 4 consecutive output columns of one output row.
 #pragma once
 
 #include "common.h"
@@ -28,7 +38,7 @@ struct KSeg {
   const uint16_t* A;   // [rows, lda] bf16
   const uint16_t* B;   // [N, ldb] bf16 (expert 0's matrix in grouped mode)
   int64_t lda, ldb;
-  int K;               // multiple of 64
+  int K;               // multiple of 32
 };
 
 struct GemmProblem {
@@ -38,7 +48,8 @@ struct GemmProblem {
   int N;                     // columns of C that are stored (multiple of 4)
   int Nb;                    // valid B rows (columns >= Nb reuse row Nb-1, results unused)
   const int32_t* gather;     // nullable: A row of output row r is gather[r]
-  const int32_t* tile_e;     // nullable: grouped mode tile table (expert of M tile)
+  const int32_t* tile_e;     // nullable: grouped mode tile table (expert of M tile);
+                             //   a grouped launch holds exactly one problem
   const int32_t* tile_m0;    //   first permuted row of M tile
   const int32_t* n_mtiles;   //   device scalar: number of valid M tiles
   const int32_t* offsets;    //   [E+1] expert row offsets
@@ -77,30 +88,61 @@ __device__ __forceinline__ void tile_order(int t, int mtiles, int ntiles, int gm
   nt = rem / gm;
 }
 
-template <int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const GemmLaunch L) {
-  constexpr int NT = 64 * WM * WN;                 // threads
-  constexpr int RS = NT / 8;                       // rows covered by one pass of 16-byte loads
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+template <int V>
+struct Stage {
+  static constexpr int value = V;
+};
+
+// slot of logical chunk c of row r (4 chunks of 16 bytes per 64-byte row)
+__device__ __forceinline__ int swz_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLaunch L) {
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  constexpr int BK = 32, CPR = 4;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;      // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;      // MFMA tiles per wave
-  constexpr int AR = BM / RS, BR = BN / RS;        // 16-byte chunks per thread per k tile
-  static_assert(TM >= 1 && TN >= 1 && AR >= 1 && BR >= 1 && BM % RS == 0 && BN % RS == 0, "tile shape");
-  __shared__ u32x4 smem[2][(BM + BN) * 8];
+  constexpr int NA = BM * CPR / (64 * NW);         // A DMA instructions per thread per k tile
+  constexpr int NB = BN * CPR / (64 * NW);
+  constexpr int PER_TILE = NA + NB;
+  constexpr int ACH = BM * CPR, BCH = BN * CPR;    // 16-byte chunks per stage
+  static_assert(TM >= 1 && TN >= 1 && NA >= 1 && NB >= 1, "tile shape");
+  static_assert(NA * 64 * NW == ACH && NB * 64 * NW == BCH, "DMA coverage");
+  __shared__ u32x4 sa0[ACH], sb0[BCH], sa1[ACH], sb1[BCH];
+  __shared__ u32x4 sa2[STAGES > 2 ? ACH : 1], sb2[STAGES > 2 ? BCH : 1];
+  __shared__ u32x4 sa3[STAGES > 3 ? ACH : 1], sb3[STAGES > 3 ? BCH : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave % WM, wave_n = wave / WM;
 
-  int bid = xcd_remap(blockIdx.x, gridDim.x);
-  int pi = 0;
-  if (L.np > 1 && bid >= L.tiles0) { pi = 1; bid -= L.tiles0; }
+  int mt, nt, pi = 0;
+  if (L.p[0].tile_e != nullptr) {
+    // grouped: the grid is sized for the most M tiles any routing can need; only
+    // the first n_mtiles * ntiles workgroups work, and the XCD renumbering runs
+    // over exactly those, so every XCD gets an equal share
+    const int mtv = *L.p[0].n_mtiles;
+    const int valid = mtv * L.p[0].ntiles;
+    if ((int)blockIdx.x >= valid) return;
+    tile_order(xcd_remap(blockIdx.x, valid), mtv, L.p[0].ntiles, L.p[0].group_m, mt, nt);
+  } else {
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    if (L.np > 1 && bid >= L.tiles0) { pi = 1; bid -= L.tiles0; }
+    tile_order(bid, L.p[pi].mtiles, L.p[pi].ntiles, L.p[pi].group_m, mt, nt);
+  }
   const GemmProblem& P = L.p[pi];
-  int mt, nt;
-  tile_order(bid, P.mtiles, P.ntiles, P.group_m, mt, nt);
 
   int m0, mend;
   int64_t b_base = 0;
   if (P.tile_e != nullptr) {
-    if (mt >= *P.n_mtiles) return;
     const int e = P.tile_e[mt];
     m0 = P.tile_m0[mt];
     mend = P.offsets[e + 1];
@@ -111,16 +153,75 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const GemmLaunc
   }
   const int n0 = nt * BN;
 
-  const int c = tid & 7, r0 = tid >> 3;
-  int64_t arow[AR];
+  // Rows and chunks this thread moves: DMA instruction i of wave w fills LDS
+  // chunks [(w*NA + i)*64, +64) of the A stage, lane l taking chunk position p.
+  int64_t arow[NA];
+  int acol[NA];
 #pragma unroll
-  for (int i = 0; i < AR; ++i) {
-    const int m = min(m0 + r0 + RS * i, mend - 1);
+  for (int i = 0; i < NA; ++i) {
+    const int p = (wave * NA + i) * 64 + lane;
+    const int r = p / CPR;
+    const int m = min(m0 + r, mend - 1);
     arow[i] = P.gather ? (int64_t)P.gather[m] : (int64_t)m;
+    acol[i] = swz_slot(r, p % CPR) * 8;
   }
-  int brow[BR];
+  int brow[NB], bcol[NB];
 #pragma unroll
-  for (int i = 0; i < BR; ++i) brow[i] = min(n0 + r0 + RS * i, P.Nb - 1);
+  for (int i = 0; i < NB; ++i) {
+    const int p = (wave * NB + i) * 64 + lane;
+    const int r = p / CPR;
+    brow[i] = min(n0 + r, P.Nb - 1);
+    bcol[i] = swz_slot(r, p % CPR) * 8;
+  }
+
+  // K segments, walked by the DMA issue in increasing tile order.
+  int nk = 0;
+  for (int s = 0; s < P.nseg; ++s) nk += P.seg[s].K / BK;
+  int seg = 0, seg_k0 = 0, seg_end = P.seg[0].K / BK;
+  const uint16_t* ap[NA];
+  const uint16_t* bp[NB];
+  auto point = [&](int s) {
+    const KSeg& S = P.seg[s];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ap[i] = S.A + arow[i] * S.lda + acol[i];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) bp[i] = S.B + b_base + (int64_t)brow[i] * S.ldb + bcol[i];
+  };
+  point(0);
+
+  auto stA = [&](auto st) -> u32x4* {
+    constexpr int v = decltype(st)::value;
+    if constexpr (v == 0) return sa0;
+    else if constexpr (v == 1) return sa1;
+    else if constexpr (v == 2) return sa2;
+    else return sa3;
+  };
+  auto stB = [&](auto st) -> u32x4* {
+    constexpr int v = decltype(st)::value;
+    if constexpr (v == 0) return sb0;
+    else if constexpr (v == 1) return sb1;
+    else if constexpr (v == 2) return sb2;
+    else return sb3;
+  };
+  auto issue = [&](int kt, auto st) {
+    while (kt >= seg_end) {          // uniform; at most nseg-1 times in the whole loop
+      seg_k0 = seg_end;
+      ++seg;
+      seg_end += P.seg[seg].K / BK;
+      point(seg);
+    }
+    const int koff = (kt - seg_k0) * BK;
+    u32x4* a = stA(st);
+    u32x4* b = stB(st);
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(ap[i] + koff), (lds_void_ptr)&a[(wave * NA + i) * 64], 16,
+                                       0, 0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(bp[i] + koff), (lds_void_ptr)&b[(wave * NB + i) * 64], 16,
+                                       0, 0);
+  };
 
   f32x16 acc[TN][TM];
 #pragma unroll
@@ -130,80 +231,58 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const GemmLaunc
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.f;
 
-  u32x4 ra[AR], rb[BR];
-  const u32x4* ap[AR];
-  const u32x4* bp[BR];
-
-  for (int s = 0; s < P.nseg; ++s) {
-    const KSeg S = P.seg[s];
+  auto step = [&](int kt, auto st) {
+    constexpr int S = decltype(st)::value;
+    MOE_WAIT_VMCNT((STAGES - 2) * PER_TILE);
+    // bare barrier: the wait above covers this wave's DMA of tile kt, the barrier
+    // everyone else's, and every wave is done with the stage refilled below
+    asm volatile("s_barrier" ::: "memory");
+    issue(min(kt + STAGES - 1, nk - 1), Stage<(S + STAGES - 1) % STAGES>{});
+    const u32x4* a = stA(st);
+    const u32x4* b = stB(st);
 #pragma unroll
-    for (int i = 0; i < AR; ++i) ap[i] = reinterpret_cast<const u32x4*>(S.A + arow[i] * S.lda + c * 8);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = ks * 2 + (lane >> 5);
+      bf16x8 af[TM], bf[TN];
 #pragma unroll
-    for (int i = 0; i < BR; ++i)
-      bp[i] = reinterpret_cast<const u32x4*>(S.B + b_base + (int64_t)brow[i] * S.ldb + c * 8);
-    const int nk = S.K / 64;
-
-#pragma unroll
-    for (int i = 0; i < AR; ++i) ra[i] = ap[i][0];
-#pragma unroll
-    for (int i = 0; i < BR; ++i) rb[i] = bp[i][0];
-#pragma unroll
-    for (int i = 0; i < AR; ++i) {
-      const int r = r0 + RS * i;
-      smem[0][r * 8 + (c ^ (r & 7))] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BR; ++i) {
-      const int r = r0 + RS * i;
-      smem[0][BM * 8 + r * 8 + (c ^ (r & 7))] = rb[i];
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        // a k tile is 64 bf16 = 8 chunks of 16 bytes
-#pragma unroll
-        for (int i = 0; i < AR; ++i) ra[i] = ap[i][(kt + 1) * 8];
-#pragma unroll
-        for (int i = 0; i < BR; ++i) rb[i] = bp[i][(kt + 1) * 8];
+      for (int tm = 0; tm < TM; ++tm) {
+        const int r = wave_m * WTM + tm * 32 + (lane & 31);
+        af[tm] = __builtin_bit_cast(bf16x8, a[r * CPR + swz_slot(r, ch)]);
       }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int ch = ks * 2 + (lane >> 5);
-        bf16x8 af[TM], bf[TN];
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const int r = wave_m * WTM + tm * 32 + (lane & 31);
-          af[tm] = __builtin_bit_cast(bf16x8, smem[cur][r * 8 + (ch ^ (r & 7))]);
-        }
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int r = wave_n * WTN + tn * 32 + (lane & 31);
-          bf[tn] = __builtin_bit_cast(bf16x8, smem[cur][BM * 8 + r * 8 + (ch ^ (r & 7))]);
-        }
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm)
-            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
+      for (int tn = 0; tn < TN; ++tn) {
+        const int r = wave_n * WTN + tn * 32 + (lane & 31);
+        bf[tn] = __builtin_bit_cast(bf16x8, b[r * CPR + swz_slot(r, ch)]);
       }
-      if (more) {
 #pragma unroll
-        for (int i = 0; i < AR; ++i) {
-          const int r = r0 + RS * i;
-          smem[cur ^ 1][r * 8 + (c ^ (r & 7))] = ra[i];
-        }
+      for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-        for (int i = 0; i < BR; ++i) {
-          const int r = r0 + RS * i;
-          smem[cur ^ 1][BM * 8 + r * 8 + (c ^ (r & 7))] = rb[i];
-        }
-      }
-      __syncthreads();
+        for (int tm = 0; tm < TM; ++tm)
+          acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
     }
+  };
+
+  issue(0, Stage<0>{});
+  if constexpr (STAGES > 2) issue(min(1, nk - 1), Stage<1>{});
+  if constexpr (STAGES > 3) issue(min(2, nk - 1), Stage<2>{});
+  // The unrolled body has no conditional steps (the compiler's wait analysis then
+  // sees the same DMA history on every trip); the remainder runs after it.
+  const int nfull = nk - nk % STAGES;
+  for (int kt = 0; kt < nfull; kt += STAGES) {
+    step(kt, Stage<0>{});
+    step(kt + 1, Stage<1>{});
+    if constexpr (STAGES > 2) step(kt + 2, Stage<2>{});
+    if constexpr (STAGES > 3) step(kt + 3, Stage<3>{});
   }
+  {
+    const int r = nk - nfull;
+    if (r > 0) step(nfull, Stage<0>{});
+    if constexpr (STAGES > 2)
+      if (r > 1) step(nfull + 1, Stage<1>{});
+    if constexpr (STAGES > 3)
+      if (r > 2) step(nfull + 2, Stage<2>{});
+  }
+  MOE_WAIT_VMCNT(0);   // no DMA may still be writing this workgroup's LDS when it ends
 
   // Epilogue: lane owns row m = (lane & 31) of each MFMA tile and, for g = 0..3,
   // the four columns 8g + 4*(lane >> 5) + 0..3.

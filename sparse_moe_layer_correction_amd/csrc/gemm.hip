@@ -19,9 +19,9 @@ hipError_t launch_gemm(GemmLaunch& L, int cfg, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   const dim3 grid((unsigned)total);
   switch (cfg) {
-    case TILE_256x256: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4>), grid, dim3(512), 0, st, L); break;
-    case TILE_128x128: hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2>), grid, dim3(256), 0, st, L); break;
-    case TILE_64x256: hipLaunchKernelGGL((gemm_bf16_kernel<64, 256, 1, 4>), grid, dim3(256), 0, st, L); break;
+    case TILE_256x256: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4>), grid, dim3(512), 0, st, L); break;
+    case TILE_128x128: hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 4>), grid, dim3(256), 0, st, L); break;
+    case TILE_64x256: hipLaunchKernelGGL((gemm_bf16_kernel<64, 256, 1, 4, 4>), grid, dim3(256), 0, st, L); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

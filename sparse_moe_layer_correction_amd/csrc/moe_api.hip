@@ -123,16 +123,27 @@ void add_seg(GemmProblem& p, const uint16_t* A, int64_t lda, const uint16_t* B, 
   p.seg[p.nseg++] = KSeg{A, B, lda, ldb, K};
 }
 
+// 256x256 tiles when they alone fill the 256 CUs twice over, else smaller tiles
+// (the router's N = E is narrow, decode's M is a few rows).
 int choose_dense_cfg(int M, int N) {
-  if (M >= 256 && N >= 256) return TILE_256x256;
+  const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  if (M >= 256 && N >= 256 && big >= 512) return TILE_256x256;
   if (M <= 64 && N >= 256) return TILE_64x256;
   return TILE_128x128;
 }
 
+// Records events[phase] (if any) on the stream.
+struct Marks {
+  hipEvent_t* ev;
+  hipStream_t st;
+  hipError_t mark(int phase) const { return ev ? hipEventRecord(ev[phase], st) : hipSuccess; }
+};
+
 int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float* w_router, const float* bias,
-              int32_t* idx, float* gate, float* gap, void* ws, hipStream_t st) {
+              int32_t* idx, float* gate, float* gap, void* ws, hipStream_t st, const Marks& mk = Marks{nullptr, 0}) {
   uint16_t* parts = at<uint16_t>(ws, l.wsplit);
   float* logits = at<float>(ws, l.logits);
+  if (mk.mark(MOE_PHASE_ROUTER_SPLIT) != hipSuccess) return MOE_ERR_HIP;
   hipError_t e = launch_split_router_weight(w_router, d.E, d.H, parts, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int cfg = choose_dense_cfg(d.T, (int)l.ldl);
@@ -141,8 +152,10 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   L.p[0] = dense_problem(cfg, d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32);
   const int64_t EH = (int64_t)d.E * d.H;
   for (int s = 0; s < 3; ++s) add_seg(L.p[0], x, d.H, parts + s * EH, d.H, d.H);
+  if (mk.mark(MOE_PHASE_ROUTER_GEMM) != hipSuccess) return MOE_ERR_HIP;
   e = launch_gemm(L, cfg, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (mk.mark(MOE_PHASE_TOPK) != hipSuccess) return MOE_ERR_HIP;
   e = launch_topk(logits, l.ldl, bias, d.T, d.E, d.K, d.routed_scaling, idx, gate, gap, st);
   return hip_status(e);
 }
@@ -242,8 +255,12 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* s
   return hip_status(e);
 }
 
-int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
-                size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
+                 size_t ws_bytes, hipStream_t stream, const Marks& mk) {
   int st;
   if (!dims_ok(dims, &st)) return st;
   if (!w || !x || !out || !w->w_router || !w->corr_bias || !w->w_fc1 || !w->w_up || !w->w_down || !w->w_fc2 ||
@@ -266,11 +283,12 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, u
   uint16_t* y_lat = at<uint16_t>(ws, l.y_lat);
 
   // 1. router
-  int rc = run_route(d, l, x, w->w_router, w->corr_bias, idx, gate, at<float>(ws, l.gap), ws, stream);
+  int rc = run_route(d, l, x, w->w_router, w->corr_bias, idx, gate, at<float>(ws, l.gap), ws, stream, mk);
   if (rc != MOE_OK) return rc;
 
   // 2. permutation maps and the M-tile table of the grouped products
   const PermuteScratch ps = permute_scratch(l, ws, 0);
+  if (mk.mark(MOE_PHASE_PERMUTE) != hipSuccess) return MOE_ERR_HIP;
   if (launch_permute_maps(idx, d.T, d.K, d.E, kGroupedBM, ps, offsets, row_token, slot_row, stream) != hipSuccess)
     return MOE_ERR_HIP;
 
@@ -283,6 +301,7 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, u
     add_seg(G.p[0], x, H, w->w_fc1, H, d.H);
     G.p[1] = dense_problem(cfg, d.T, d.Is, d.Is, hs, Is, EPI_RELU2_BF16);
     add_seg(G.p[1], x, H, w->w_sh_up, H, d.H);
+    if (mk.mark(MOE_PHASE_FC1_SHARED_UP) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm(G, cfg, stream) != hipSuccess) return MOE_ERR_HIP;
   }
 
@@ -307,6 +326,7 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, u
     p.ntiles = (d.I + ts.BN - 1) / ts.BN;
     p.group_m = 4;
     add_seg(p, z, L, w->w_up, L, d.L);
+    if (mk.mark(MOE_PHASE_EXPERT_UP) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm(G, kGroupedCfg, stream) != hipSuccess) return MOE_ERR_HIP;
   }
 
@@ -330,10 +350,12 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, u
     p.ntiles = (d.L + ts.BN - 1) / ts.BN;
     p.group_m = 4;
     add_seg(p, h, I, w->w_down, I, d.I);
+    if (mk.mark(MOE_PHASE_EXPERT_DOWN) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm(G, kGroupedCfg, stream) != hipSuccess) return MOE_ERR_HIP;
   }
 
   // 6. gate-weighted combine in the latent
+  if (mk.mark(MOE_PHASE_COMBINE) != hipSuccess) return MOE_ERR_HIP;
   if (launch_combine(y, gate, slot_row, d.T, d.K, d.L, y_lat, stream) != hipSuccess) return MOE_ERR_HIP;
 
   // 7. out = y_lat . W_fc2^T + hs . W_sd^T, one fp32 accumulator, one rounding
@@ -344,10 +366,29 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, u
     G.p[0] = dense_problem(cfg, d.T, d.H, d.H, out, H, EPI_BF16);
     add_seg(G.p[0], y_lat, L, w->w_fc2, L, d.L);
     add_seg(G.p[0], hs, Is, w->w_sh_down, Is, d.Is);
+    if (mk.mark(MOE_PHASE_FC2_SHARED_DOWN) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm(G, cfg, stream) != hipSuccess) return MOE_ERR_HIP;
   }
+  if (mk.mark(MOE_N_PHASES) != hipSuccess) return MOE_ERR_HIP;
   (void)TK;
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  return forward_impl(dims, w, x, out, ws, ws_bytes, stream, Marks{nullptr, stream});
+}
+
+int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
+                         size_t ws_bytes, hipStream_t stream, hipEvent_t* events, int n_events) {
+  if (events == nullptr || n_events < MOE_N_PHASES + 1) return MOE_ERR_INVALID;
+  for (int i = 0; i <= MOE_N_PHASES; ++i)
+    if (events[i] == nullptr) return MOE_ERR_INVALID;
+  return forward_impl(dims, w, x, out, ws, ws_bytes, stream, Marks{events, stream});
 }
 
 }  // extern "C"
