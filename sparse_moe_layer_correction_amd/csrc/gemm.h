@@ -105,7 +105,7 @@ __device__ __forceinline__ int swz_slot(int r, int c) { return c ^ ((r >> 2) & 3
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLaunch L) {
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(STAGES >= 2 && STAGES <= 5, "stages");
   constexpr int BK = 32, CPR = 4;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;      // wave tile
@@ -119,6 +119,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
   __shared__ u32x4 sa0[ACH], sb0[BCH], sa1[ACH], sb1[BCH];
   __shared__ u32x4 sa2[STAGES > 2 ? ACH : 1], sb2[STAGES > 2 ? BCH : 1];
   __shared__ u32x4 sa3[STAGES > 3 ? ACH : 1], sb3[STAGES > 3 ? BCH : 1];
+  __shared__ u32x4 sa4[STAGES > 4 ? ACH : 1], sb4[STAGES > 4 ? BCH : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,14 +195,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
     if constexpr (v == 0) return sa0;
     else if constexpr (v == 1) return sa1;
     else if constexpr (v == 2) return sa2;
-    else return sa3;
+    else if constexpr (v == 3) return sa3;
+    else return sa4;
   };
   auto stB = [&](auto st) -> u32x4* {
     constexpr int v = decltype(st)::value;
     if constexpr (v == 0) return sb0;
     else if constexpr (v == 1) return sb1;
     else if constexpr (v == 2) return sb2;
-    else return sb3;
+    else if constexpr (v == 3) return sb3;
+    else return sb4;
   };
   auto issue = [&](int kt, auto st) {
     while (kt >= seg_end) {          // uniform; at most nseg-1 times in the whole loop
@@ -265,6 +268,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
   issue(0, Stage<0>{});
   if constexpr (STAGES > 2) issue(min(1, nk - 1), Stage<1>{});
   if constexpr (STAGES > 3) issue(min(2, nk - 1), Stage<2>{});
+  if constexpr (STAGES > 4) issue(min(3, nk - 1), Stage<3>{});
   // The unrolled body has no conditional steps (the compiler's wait analysis then
   // sees the same DMA history on every trip); the remainder runs after it.
   const int nfull = nk - nk % STAGES;
@@ -273,6 +277,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
     step(kt + 1, Stage<1>{});
     if constexpr (STAGES > 2) step(kt + 2, Stage<2>{});
     if constexpr (STAGES > 3) step(kt + 3, Stage<3>{});
+    if constexpr (STAGES > 4) step(kt + 4, Stage<4>{});
   }
   {
     const int r = nk - nfull;
@@ -281,6 +286,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
       if (r > 1) step(nfull + 1, Stage<1>{});
     if constexpr (STAGES > 3)
       if (r > 2) step(nfull + 2, Stage<2>{});
+    if constexpr (STAGES > 4)
+      if (r > 3) step(nfull + 3, Stage<3>{});
   }
   MOE_WAIT_VMCNT(0);   // no DMA may still be writing this workgroup's LDS when it ends
 

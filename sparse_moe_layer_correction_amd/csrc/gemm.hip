@@ -8,6 +8,7 @@ TileShape tile_shape(int cfg) {
     case TILE_256x256: return {256, 256};
     case TILE_128x128: return {128, 128};
     case TILE_64x256: return {64, 256};
+    case TILE_256x256_DEEP: return {256, 256};
     default: return {0, 0};
   }
 }
@@ -22,6 +23,9 @@ hipError_t launch_gemm(GemmLaunch& L, int cfg, hipStream_t st) {
     case TILE_256x256: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4>), grid, dim3(512), 0, st, L); break;
     case TILE_128x128: hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 4>), grid, dim3(256), 0, st, L); break;
     case TILE_64x256: hipLaunchKernelGGL((gemm_bf16_kernel<64, 256, 1, 4, 4>), grid, dim3(256), 0, st, L); break;
+    // five stages fill the whole 160 KB of LDS: one more tile in flight for
+    // operands that stream cold from HBM (expert weights)
+    case TILE_256x256_DEEP: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 5>), grid, dim3(512), 0, st, L); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -12,12 +12,33 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 
 // GEMM tile configurations (BM x BN; 256x256 runs 8 waves, the others 4).
-enum TileCfg : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x256 = 2, TILE_COUNT = 3 };
+enum TileCfg : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x256 = 2, TILE_256x256_DEEP = 3, TILE_COUNT = 4 };
 struct TileShape { int BM, BN; };
 TileShape tile_shape(int cfg);
 
 // Fills mtiles/ntiles-independent fields; the caller sets the problem fields.
 hipError_t launch_gemm(GemmLaunch& L, int cfg, hipStream_t st);
+
+// Few-row (decode) product streamed straight from HBM, see skinny.hip.
+struct SkinnyProblem {
+  KSeg seg[3];
+  int nseg;
+  int M;                     // dense rows (rows of the split-K partials)
+  int N, Nb;                 // stored columns (multiple of 4), valid B rows
+  int groups;                // 1 for a dense product; grouped: an upper bound on the experts listed
+  const int32_t* offsets;    // grouped: [E+1] permuted row offsets (nullable -> dense)
+  const int32_t* group_list; // grouped: the experts to run (those with tokens)
+  const int32_t* n_groups;   // grouped: device scalar, length of group_list
+  const int32_t* gather;     // nullable: A row of output row r is gather[r]
+  int64_t b_estride;         // grouped: elements between experts' B
+  void* C;
+  int64_t ldc;
+  int epi;
+  int ksplit;                // dense: K split over this many waves per slab
+  float* partial;            // [ksplit, M, N] fp32 when ksplit > 1, else null
+};
+hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st);
+int skinny_slabs_per_wave(const SkinnyProblem& P);
 
 struct PermuteScratch {
   uint64_t* masks;     // [E][nblk]
@@ -26,6 +47,8 @@ struct PermuteScratch {
   int32_t* tile_e;     // [max_mtiles]
   int32_t* tile_m0;    // [max_mtiles]
   int32_t* n_mtiles;   // [1]
+  int32_t* touched;    // [E] experts with at least one token, ascending
+  int32_t* n_touched;  // [1]
 };
 
 hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* parts, hipStream_t st);

@@ -16,16 +16,34 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Tile shape of the grouped expert products; the permutation lays out the
 // M-tile table for this BM.
-constexpr int kGroupedCfg = TILE_256x256;
+constexpr int kGroupedCfg = TILE_256x256_DEEP;
 constexpr int kGroupedBM = 256;
+
+// Up to this many tokens the products stream their weights with the skinny
+// (few-row) kernels instead of the tiled MFMA GEMM.
+constexpr int kSkinnyMaxT = 64;
+// Dense skinny products split K until about this many waves are in flight.
+constexpr int kSkinnyTargetWaves = 2048;
+
+int skinny_ksplit(int N, int K, int M) {
+  if (N <= 0 || K < 32) return 1;
+  const int width = M > 16 ? 64 : 16;      // columns per wave (see skinny_slabs_per_wave)
+  const int slabs = (N + width - 1) / width;
+  int ks = (kSkinnyTargetWaves + slabs - 1) / slabs;
+  // the fp32 partials are written once and read once: 8*ks*M*N bytes against
+  // 2*N*K bytes of weights; keep them within a quarter of the weight traffic
+  const int cap = std::max(1, K / (16 * std::max(M, 1)));
+  ks = std::max(1, std::min(std::min(ks, cap), K / 32));
+  return ks;
+}
 
 struct Layout {
   // route
   size_t wsplit, logits;
   // permute
-  size_t masks, base, counts, tile_e, tile_m0, n_mtiles;
+  size_t masks, base, counts, tile_e, tile_m0, n_mtiles, touched, n_touched;
   // forward
-  size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat;
+  size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial;
   size_t route_end, permute_begin, permute_end, total;
   int64_t ldl;         // logits row stride (E rounded up to 64)
   int nblk;            // token blocks of 64
@@ -78,6 +96,8 @@ Layout make_layout(const moe_dims& d) {
   l.tile_e = take((size_t)l.max_mtiles * 4);
   l.tile_m0 = take((size_t)l.max_mtiles * 4);
   l.n_mtiles = take(4);
+  l.touched = take(E * 4);
+  l.n_touched = take(4);
   l.permute_end = o;
   l.idx = take(TK * 4);
   l.gate = take(TK * 4);
@@ -90,6 +110,16 @@ Layout make_layout(const moe_dims& d) {
   l.h = take(TK * I * 2);
   l.y = take(TK * L * 2);
   l.y_lat = take(T * L * 2);
+  l.partial = o;
+  if (T <= kSkinnyMaxT && L > 0 && I > 0 && Is > 0 && H > 0) {
+    // split-K partials of the dense skinny products: [ksplit, T, N] fp32
+    size_t p = 0;
+    p = std::max(p, (size_t)skinny_ksplit((int)l.ldl, (int)(3 * H), (int)T) * T * l.ldl * 4);
+    p = std::max(p, (size_t)skinny_ksplit((int)L, (int)H, (int)T) * T * L * 4);
+    p = std::max(p, (size_t)skinny_ksplit((int)Is, (int)H, (int)T) * T * Is * 4);
+    p = std::max(p, (size_t)skinny_ksplit((int)H, (int)(L + Is), (int)T) * T * H * 4);
+    take(p);
+  }
   l.total = o;
   return l;
 }
@@ -123,6 +153,46 @@ void add_seg(GemmProblem& p, const uint16_t* A, int64_t lda, const uint16_t* B, 
   p.seg[p.nseg++] = KSeg{A, B, lda, ldb, K};
 }
 
+void add_seg(SkinnyProblem& p, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int K) {
+  p.seg[p.nseg++] = KSeg{A, B, lda, ldb, K};
+}
+
+// Dense skinny problem C[M, N] over a total reduction length Ktot.
+SkinnyProblem skinny_dense(int M, int N, int Nb, void* C, int64_t ldc, int epi, int Ktot, float* partial) {
+  SkinnyProblem p{};
+  p.M = M;
+  p.N = N;
+  p.Nb = Nb;
+  p.groups = 1;
+  p.C = C;
+  p.ldc = ldc;
+  p.epi = epi;
+  p.ksplit = skinny_ksplit(N, Ktot, M);
+  p.partial = p.ksplit > 1 ? partial : nullptr;
+  if (p.partial == nullptr) p.ksplit = 1;
+  return p;
+}
+
+// Grouped skinny problem over the permuted rows of each expert that has tokens;
+// at most min(E, T*K) experts can.
+SkinnyProblem skinny_grouped(int max_groups, const PermuteScratch& ps, int N, const int32_t* offsets,
+                             const int32_t* gather, int64_t b_estride, void* C, int64_t ldc, int epi) {
+  SkinnyProblem p{};
+  p.N = N;
+  p.Nb = N;
+  p.groups = max_groups;
+  p.group_list = ps.touched;
+  p.n_groups = ps.n_touched;
+  p.offsets = offsets;
+  p.gather = gather;
+  p.b_estride = b_estride;
+  p.C = C;
+  p.ldc = ldc;
+  p.epi = epi;
+  p.ksplit = 1;
+  return p;
+}
+
 // 256x256 tiles when they alone fill the 256 CUs twice over, else smaller tiles
 // (the router's N = E is narrow, decode's M is a few rows).
 int choose_dense_cfg(int M, int N) {
@@ -140,20 +210,27 @@ struct Marks {
 };
 
 int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float* w_router, const float* bias,
-              int32_t* idx, float* gate, float* gap, void* ws, hipStream_t st, const Marks& mk = Marks{nullptr, 0}) {
+              int32_t* idx, float* gate, float* gap, void* ws, hipStream_t st, const Marks& mk = Marks{nullptr, 0},
+              float* partial = nullptr) {
   uint16_t* parts = at<uint16_t>(ws, l.wsplit);
   float* logits = at<float>(ws, l.logits);
   if (mk.mark(MOE_PHASE_ROUTER_SPLIT) != hipSuccess) return MOE_ERR_HIP;
   hipError_t e = launch_split_router_weight(w_router, d.E, d.H, parts, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  const int cfg = choose_dense_cfg(d.T, (int)l.ldl);
-  GemmLaunch L{};
-  L.np = 1;
-  L.p[0] = dense_problem(cfg, d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32);
   const int64_t EH = (int64_t)d.E * d.H;
-  for (int s = 0; s < 3; ++s) add_seg(L.p[0], x, d.H, parts + s * EH, d.H, d.H);
   if (mk.mark(MOE_PHASE_ROUTER_GEMM) != hipSuccess) return MOE_ERR_HIP;
-  e = launch_gemm(L, cfg, st);
+  if (d.T <= kSkinnyMaxT && partial != nullptr) {
+    SkinnyProblem P = skinny_dense(d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32, 3 * d.H, partial);
+    for (int s = 0; s < 3; ++s) add_seg(P, x, d.H, parts + s * EH, d.H, d.H);
+    e = launch_skinny(P, st);
+  } else {
+    const int cfg = choose_dense_cfg(d.T, (int)l.ldl);
+    GemmLaunch L{};
+    L.np = 1;
+    L.p[0] = dense_problem(cfg, d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32);
+    for (int s = 0; s < 3; ++s) add_seg(L.p[0], x, d.H, parts + s * EH, d.H, d.H);
+    e = launch_gemm(L, cfg, st);
+  }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (mk.mark(MOE_PHASE_TOPK) != hipSuccess) return MOE_ERR_HIP;
   e = launch_topk(logits, l.ldl, bias, d.T, d.E, d.K, d.routed_scaling, idx, gate, gap, st);
@@ -163,8 +240,9 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
 // The permute scratch of a workspace whose first byte sits at layout offset `origin`.
 PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
   return PermuteScratch{at<uint64_t>(ws, l.masks - origin), at<int32_t>(ws, l.base - origin),
-                        at<int32_t>(ws, l.counts - origin), at<int32_t>(ws, l.tile_e - origin),
-                        at<int32_t>(ws, l.tile_m0 - origin), at<int32_t>(ws, l.n_mtiles - origin)};
+                        at<int32_t>(ws, l.counts - origin),   at<int32_t>(ws, l.tile_e - origin),
+                        at<int32_t>(ws, l.tile_m0 - origin),  at<int32_t>(ws, l.n_mtiles - origin),
+                        at<int32_t>(ws, l.touched - origin),  at<int32_t>(ws, l.n_touched - origin)};
 }
 
 }  // namespace
@@ -283,7 +361,9 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   uint16_t* y_lat = at<uint16_t>(ws, l.y_lat);
 
   // 1. router
-  int rc = run_route(d, l, x, w->w_router, w->corr_bias, idx, gate, at<float>(ws, l.gap), ws, stream, mk);
+  const bool skinny = d.T <= kSkinnyMaxT;
+  float* partial = skinny ? at<float>(ws, l.partial) : nullptr;
+  int rc = run_route(d, l, x, w->w_router, w->corr_bias, idx, gate, at<float>(ws, l.gap), ws, stream, mk, partial);
   if (rc != MOE_OK) return rc;
 
   // 2. permutation maps and the M-tile table of the grouped products
@@ -293,7 +373,15 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     return MOE_ERR_HIP;
 
   // 3. x read by one launch for fc1 (z) and the shared expert's up + relu^2 (hs)
-  {
+  if (skinny) {
+    if (mk.mark(MOE_PHASE_FC1_SHARED_UP) != hipSuccess) return MOE_ERR_HIP;
+    SkinnyProblem P = skinny_dense(d.T, d.L, d.L, z, L, EPI_BF16, d.H, partial);
+    add_seg(P, x, H, w->w_fc1, H, d.H);
+    if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
+    SkinnyProblem Q = skinny_dense(d.T, d.Is, d.Is, hs, Is, EPI_RELU2_BF16, d.H, partial);
+    add_seg(Q, x, H, w->w_sh_up, H, d.H);
+    if (launch_skinny(Q, stream) != hipSuccess) return MOE_ERR_HIP;
+  } else {
     const int cfg = choose_dense_cfg(d.T, std::min(d.L, d.Is));
     GemmLaunch G{};
     G.np = 2;
@@ -306,7 +394,13 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   }
 
   // 4. expert up + relu^2 over the permuted rows; z rows gathered on load
-  {
+  if (skinny) {
+    if (mk.mark(MOE_PHASE_EXPERT_UP) != hipSuccess) return MOE_ERR_HIP;
+    SkinnyProblem P = skinny_grouped(std::min(d.E, d.T * d.K), ps, d.I, offsets, row_token, I * L, h, I,
+                                     EPI_RELU2_BF16);
+    add_seg(P, z, L, w->w_up, L, d.L);
+    if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
+  } else {
     const TileShape ts = tile_shape(kGroupedCfg);
     GemmLaunch G{};
     G.np = 1;
@@ -331,7 +425,12 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   }
 
   // 5. expert down over the permuted rows
-  {
+  if (skinny) {
+    if (mk.mark(MOE_PHASE_EXPERT_DOWN) != hipSuccess) return MOE_ERR_HIP;
+    SkinnyProblem P = skinny_grouped(std::min(d.E, d.T * d.K), ps, d.L, offsets, nullptr, L * I, y, L, EPI_BF16);
+    add_seg(P, h, I, w->w_down, I, d.I);
+    if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
+  } else {
     const TileShape ts = tile_shape(kGroupedCfg);
     GemmLaunch G{};
     G.np = 1;
@@ -359,7 +458,13 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   if (launch_combine(y, gate, slot_row, d.T, d.K, d.L, y_lat, stream) != hipSuccess) return MOE_ERR_HIP;
 
   // 7. out = y_lat . W_fc2^T + hs . W_sd^T, one fp32 accumulator, one rounding
-  {
+  if (skinny) {
+    if (mk.mark(MOE_PHASE_FC2_SHARED_DOWN) != hipSuccess) return MOE_ERR_HIP;
+    SkinnyProblem P = skinny_dense(d.T, d.H, d.H, out, H, EPI_BF16, d.L + d.Is, partial);
+    add_seg(P, y_lat, L, w->w_fc2, L, d.L);
+    add_seg(P, hs, Is, w->w_sh_down, Is, d.Is);
+    if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
+  } else {
     const int cfg = choose_dense_cfg(d.T, d.H);
     GemmLaunch G{};
     G.np = 1;

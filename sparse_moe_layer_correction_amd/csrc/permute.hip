@@ -50,32 +50,40 @@ __global__ void __launch_bounds__(256) expert_scan_kernel(const uint64_t* __rest
 }
 
 // One workgroup of 1024 threads (E <= 1024).
+// One workgroup of 1024 threads (E <= 1024). Also lists the experts that
+// received at least one token, in ascending order.
 __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict__ counts, int E, int BM,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ tile_e,
                                                        int32_t* __restrict__ tile_m0,
-                                                       int32_t* __restrict__ n_mtiles) {
-  __shared__ int wsum_c[16], wsum_t[16];
+                                                       int32_t* __restrict__ n_mtiles,
+                                                       int32_t* __restrict__ touched,
+                                                       int32_t* __restrict__ n_touched) {
+  __shared__ int wsum_c[16], wsum_t[16], wsum_h[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid < E ? counts[tid] : 0;
   const int nt = (c + BM - 1) / BM;
+  const int hit = c > 0 ? 1 : 0;
   const int ic = wave_inclusive_scan_i32(c);
   const int it = wave_inclusive_scan_i32(nt);
-  if (lane == 63) { wsum_c[wave] = ic; wsum_t[wave] = it; }
+  const int ih = wave_inclusive_scan_i32(hit);
+  if (lane == 63) { wsum_c[wave] = ic; wsum_t[wave] = it; wsum_h[wave] = ih; }
   __syncthreads();
-  int pc = 0, pt = 0;
-  for (int w = 0; w < wave; ++w) { pc += wsum_c[w]; pt += wsum_t[w]; }
-  const int ex_c = pc + ic - c, ex_t = pt + it - nt;
+  int pc = 0, pt = 0, ph = 0;
+  for (int w = 0; w < wave; ++w) { pc += wsum_c[w]; pt += wsum_t[w]; ph += wsum_h[w]; }
+  const int ex_c = pc + ic - c, ex_t = pt + it - nt, ex_h = ph + ih - hit;
   if (tid < E) {
     offsets[tid] = ex_c;
     for (int i = 0; i < nt; ++i) {
       tile_e[ex_t + i] = tid;
       tile_m0[ex_t + i] = ex_c + i * BM;
     }
+    if (hit) touched[ex_h] = tid;
   }
   if (tid == E - 1) {
     offsets[E] = ex_c + c;
     *n_mtiles = ex_t + nt;
+    *n_touched = ex_h + hit;
   }
 }
 
@@ -119,7 +127,7 @@ hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, 
   hipLaunchKernelGGL(block_masks_kernel, dim3(nblk), dim3(256), 0, st, idx, T, K, E, nblk, ps.masks);
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, st, ps.masks, nblk, E, ps.base, ps.counts);
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, ps.counts, E, BM, offsets, ps.tile_e, ps.tile_m0,
-                     ps.n_mtiles);
+                     ps.n_mtiles, ps.touched, ps.n_touched);
   const int64_t tk = (int64_t)T * K;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st, idx, T, K, E, nblk,
                      ps.masks, ps.base, offsets, row_token, slot_row);

@@ -73,11 +73,23 @@ def test_workspace_sizes(lib):
     assert 0 < lib.moe_permute_workspace_bytes(_d(ULTRA)) < 10e6
 
 
-def test_partial_calls_read_only_their_fields(lib):
-    d = M.MoEDims(100, 128, 0, 40, 0, 5, 0)
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 100])
+def test_partial_calls_read_only_their_fields(lib, T):
+    d = M.MoEDims(T, 128, 0, 40, 0, 5, 0)
     assert lib.moe_route_workspace_bytes(_d(d)) > 0
     assert lib.moe_permute_workspace_bytes(_d(d)) > 0
     assert lib.moe_workspace_bytes(_d(d)) == 0          # the forward needs L, I, Is
+
+
+@pytest.mark.parametrize("T", [1, 7, 64, 65, 16384])
+def test_workspace_sizes_at_every_token_count(lib, T):
+    """Few-token forwards carry split-K partials; every size stays consistent."""
+    d = M.MoEDims(T, 8192, 2048, 512, 5120, 22, 10240, 5.0)
+    n = lib.moe_workspace_bytes(_d(d))
+    lay = M.workspace_layout(d)
+    assert n == lay["total"] > 0
+    assert lay["y_lat"] + T * 2048 * 2 <= n
+    assert lib.moe_route_workspace_bytes(_d(d)) < n
 
 
 @pytest.mark.parametrize("bad,code", [

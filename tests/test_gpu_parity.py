@@ -165,7 +165,10 @@ def _compare_tokens(d, out, ws, lay, tokens, idx_gpu, label):
 
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", dict(T=37)), ("tiny", dict(T=1)),
-                                       ("tiny", dict(K=16)), ("tiny", dict(K=1))])
+                                       ("tiny", dict(K=16)), ("tiny", dict(K=1)),
+                                       # above the few-token threshold: the tiled GEMM path
+                                       ("tiny", dict(T=300)), ("tiny", dict(T=65, K=16)),
+                                       ("tiny", dict(T=777, K=1))])
 def test_forward_tiny_full(name, over):
     d = device_inputs(name, **over)
     cfg = d["cfg"]
