@@ -12,7 +12,6 @@ of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -25,15 +24,6 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "LatentMoE fwd tokens/s + TFLOP/s (Ultra shape); % MFMA peak / % HBM BW"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ("gemm.h", "common.h")
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_moe_layer_correction_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def phase_work(cfg, n_touched: int):
@@ -92,6 +82,8 @@ def main():
                     choices=["ultra_prefill", "ultra_decode64", "ultra_decode1", "nano", "super", "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -147,12 +139,14 @@ def main():
     dur_s = phase_ms[dom] / 1e3
     traffic = None
     try:
+        from sparse_moe_layer_correction_amd.profiling import kernel_source_hash
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        rec = tr.get(cfg.name, {}).get(dom)
-        if rec and rec.get("kernel_hash") == kernel_source_hash():
+        rec = tr.get(cfg.name, {}).get("phases", {}).get(dom)
+        family = "skinny" if cfg.T <= 64 else "gemm"
+        if rec and rec.get("kernel_hash") == kernel_source_hash(family):
             traffic = rec["bytes_per_launch"]
-    except (OSError, ValueError):
+    except (OSError, ValueError, KeyError):
         pass
     if prefill:
         achieved = flops[dom] / dur_s / 1e12
@@ -193,6 +187,13 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, cfg, idx_gpu, args.cpu_tokens)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(result), flush=True)
 
 

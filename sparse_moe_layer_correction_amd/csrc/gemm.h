@@ -52,6 +52,7 @@ struct GemmProblem {
                              //   a grouped launch holds exactly one problem
   const int32_t* tile_m0;    //   first permuted row of M tile
   const int32_t* n_mtiles;   //   device scalar: number of valid M tiles
+  const int32_t* first_mtile;  // [E] each expert's first M tile in the table
   const int32_t* offsets;    //   [E+1] expert row offsets
   int64_t b_estride;         //   elements between consecutive experts' B
   void* C;
@@ -103,7 +104,8 @@ struct Stage {
 // slot of logical chunk c of row r (4 chunks of 16 bytes per 64-byte row)
 __device__ __forceinline__ int swz_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+// EPI: an Epilogue fixed at compile time, or -1 to take each problem's own.
+template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLaunch L) {
   static_assert(STAGES >= 2 && STAGES <= 5, "stages");
   constexpr int BK = 32, CPR = 4;
@@ -131,9 +133,18 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
     // the first n_mtiles * ntiles workgroups work, and the XCD renumbering runs
     // over exactly those, so every XCD gets an equal share
     const int mtv = *L.p[0].n_mtiles;
-    const int valid = mtv * L.p[0].ntiles;
+    const int ntl = L.p[0].ntiles;
+    const int valid = mtv * ntl;
     if ((int)blockIdx.x >= valid) return;
-    tile_order(xcd_remap(blockIdx.x, valid), mtv, L.p[0].ntiles, L.p[0].group_m, mt, nt);
+    // expert by expert: the tiles of one expert are contiguous in the order,
+    // M fastest, so the M tiles that share a weight panel run side by side
+    const int t = xcd_remap(blockIdx.x, valid);
+    const int e = L.p[0].tile_e[t / ntl];
+    const int f = L.p[0].first_mtile[e];
+    const int ne = (L.p[0].offsets[e + 1] - L.p[0].offsets[e] + BM - 1) / BM;
+    const int local = t - f * ntl;
+    mt = f + local % ne;
+    nt = local / ne;
   } else {
     int bid = xcd_remap(blockIdx.x, gridDim.x);
     if (L.np > 1 && bid >= L.tiles0) { pi = 1; bid -= L.tiles0; }
@@ -293,6 +304,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
 
   // Epilogue: lane owns row m = (lane & 31) of each MFMA tile and, for g = 0..3,
   // the four columns 8g + 4*(lane >> 5) + 0..3.
+  const int epi = EPI >= 0 ? EPI : P.epi;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int m = m0 + wave_m * WTM + tm * 32 + (lane & 31);
@@ -305,11 +317,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
         if (n >= P.N) continue;
         float v0 = acc[tn][tm][4 * g + 0], v1 = acc[tn][tm][4 * g + 1];
         float v2 = acc[tn][tm][4 * g + 2], v3 = acc[tn][tm][4 * g + 3];
-        if (P.epi == EPI_F32) {
+        if (epi == EPI_F32) {
           f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(P.C) + (int64_t)m * P.ldc + n);
           *dst = f32x4{v0, v1, v2, v3};
         } else {
-          if (P.epi == EPI_RELU2_BF16) {
+          if (epi == EPI_RELU2_BF16) {
             v0 = relu2(v0); v1 = relu2(v1); v2 = relu2(v2); v3 = relu2(v3);
           }
           u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n);

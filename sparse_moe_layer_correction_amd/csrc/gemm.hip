@@ -8,7 +8,7 @@ TileShape tile_shape(int cfg) {
     case TILE_256x256: return {256, 256};
     case TILE_128x128: return {128, 128};
     case TILE_64x256: return {64, 256};
-    case TILE_256x256_DEEP: return {256, 256};
+    case TILE_256x256_GROUPED: return {256, 256};
     default: return {0, 0};
   }
 }
@@ -20,12 +20,17 @@ hipError_t launch_gemm(GemmLaunch& L, int cfg, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   const dim3 grid((unsigned)total);
   switch (cfg) {
-    case TILE_256x256: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4>), grid, dim3(512), 0, st, L); break;
-    case TILE_128x128: hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 4>), grid, dim3(256), 0, st, L); break;
-    case TILE_64x256: hipLaunchKernelGGL((gemm_bf16_kernel<64, 256, 1, 4, 4>), grid, dim3(256), 0, st, L); break;
-    // five stages fill the whole 160 KB of LDS: one more tile in flight for
-    // operands that stream cold from HBM (expert weights)
-    case TILE_256x256_DEEP: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 5>), grid, dim3(512), 0, st, L); break;
+    case TILE_256x256: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, -1>), grid, dim3(512), 0, st, L); break;
+    case TILE_128x128: hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 4, -1>), grid, dim3(256), 0, st, L); break;
+    case TILE_64x256: hipLaunchKernelGGL((gemm_bf16_kernel<64, 256, 1, 4, 4, -1>), grid, dim3(256), 0, st, L); break;
+    // grouped expert products: one problem, epilogue fixed at compile time (the
+    // up and down products are then also told apart by name in profiles)
+    case TILE_256x256_GROUPED:
+      if (L.p[0].epi == EPI_RELU2_BF16)
+        hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, EPI_RELU2_BF16>), grid, dim3(512), 0, st, L);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, EPI_BF16>), grid, dim3(512), 0, st, L);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -12,7 +12,8 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 
 // GEMM tile configurations (BM x BN; 256x256 runs 8 waves, the others 4).
-enum TileCfg : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x256 = 2, TILE_256x256_DEEP = 3, TILE_COUNT = 4 };
+// TILE_256x256_GROUPED: the grouped expert products (one problem per launch).
+enum TileCfg : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x256 = 2, TILE_256x256_GROUPED = 3, TILE_COUNT = 4 };
 struct TileShape { int BM, BN; };
 TileShape tile_shape(int cfg);
 
@@ -49,6 +50,7 @@ struct PermuteScratch {
   int32_t* n_mtiles;   // [1]
   int32_t* touched;    // [E] experts with at least one token, ascending
   int32_t* n_touched;  // [1]
+  int32_t* first_mtile;  // [E] index of each expert's first M tile in the tile table
 };
 
 hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* parts, hipStream_t st);

@@ -16,7 +16,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Tile shape of the grouped expert products; the permutation lays out the
 // M-tile table for this BM.
-constexpr int kGroupedCfg = TILE_256x256_DEEP;
+constexpr int kGroupedCfg = TILE_256x256_GROUPED;
 constexpr int kGroupedBM = 256;
 
 // Up to this many tokens the products stream their weights with the skinny
@@ -41,7 +41,7 @@ struct Layout {
   // route
   size_t wsplit, logits;
   // permute
-  size_t masks, base, counts, tile_e, tile_m0, n_mtiles, touched, n_touched;
+  size_t masks, base, counts, tile_e, tile_m0, n_mtiles, touched, n_touched, first_mtile;
   // forward
   size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial;
   size_t route_end, permute_begin, permute_end, total;
@@ -98,6 +98,7 @@ Layout make_layout(const moe_dims& d) {
   l.n_mtiles = take(4);
   l.touched = take(E * 4);
   l.n_touched = take(4);
+  l.first_mtile = take(E * 4);
   l.permute_end = o;
   l.idx = take(TK * 4);
   l.gate = take(TK * 4);
@@ -242,7 +243,8 @@ PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
   return PermuteScratch{at<uint64_t>(ws, l.masks - origin), at<int32_t>(ws, l.base - origin),
                         at<int32_t>(ws, l.counts - origin),   at<int32_t>(ws, l.tile_e - origin),
                         at<int32_t>(ws, l.tile_m0 - origin),  at<int32_t>(ws, l.n_mtiles - origin),
-                        at<int32_t>(ws, l.touched - origin),  at<int32_t>(ws, l.n_touched - origin)};
+                        at<int32_t>(ws, l.touched - origin),  at<int32_t>(ws, l.n_touched - origin),
+                        at<int32_t>(ws, l.first_mtile - origin)};
 }
 
 }  // namespace
@@ -411,6 +413,7 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.tile_e = ps.tile_e;
     p.tile_m0 = ps.tile_m0;
     p.n_mtiles = ps.n_mtiles;
+    p.first_mtile = ps.first_mtile;
     p.offsets = offsets;
     p.b_estride = I * L;
     p.C = h;
@@ -440,6 +443,7 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.tile_e = ps.tile_e;
     p.tile_m0 = ps.tile_m0;
     p.n_mtiles = ps.n_mtiles;
+    p.first_mtile = ps.first_mtile;
     p.offsets = offsets;
     p.b_estride = L * I;
     p.C = y;

@@ -58,7 +58,8 @@ __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ tile_m0,
                                                        int32_t* __restrict__ n_mtiles,
                                                        int32_t* __restrict__ touched,
-                                                       int32_t* __restrict__ n_touched) {
+                                                       int32_t* __restrict__ n_touched,
+                                                       int32_t* __restrict__ first_mtile) {
   __shared__ int wsum_c[16], wsum_t[16], wsum_h[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid < E ? counts[tid] : 0;
@@ -74,6 +75,7 @@ __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict
   const int ex_c = pc + ic - c, ex_t = pt + it - nt, ex_h = ph + ih - hit;
   if (tid < E) {
     offsets[tid] = ex_c;
+    first_mtile[tid] = ex_t;
     for (int i = 0; i < nt; ++i) {
       tile_e[ex_t + i] = tid;
       tile_m0[ex_t + i] = ex_c + i * BM;
@@ -127,7 +129,7 @@ hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, 
   hipLaunchKernelGGL(block_masks_kernel, dim3(nblk), dim3(256), 0, st, idx, T, K, E, nblk, ps.masks);
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, st, ps.masks, nblk, E, ps.base, ps.counts);
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, ps.counts, E, BM, offsets, ps.tile_e, ps.tile_m0,
-                     ps.n_mtiles, ps.touched, ps.n_touched);
+                     ps.n_mtiles, ps.touched, ps.n_touched, ps.first_mtile);
   const int64_t tk = (int64_t)T * K;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st, idx, T, K, E, nblk,
                      ps.masks, ps.base, offsets, row_token, slot_row);

@@ -31,7 +31,7 @@ int skinny_slabs_per_wave(const SkinnyProblem& P) { return (P.offsets == nullptr
 template <int MT, int NS, int UNROLL>
 __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first, int rows, int row0,
                                             const int32_t* gather, int64_t b_base, int k_begin, int k_end,
-                                            int out_row0, float* partial, int lane) {
+                                            int out_row0, float* partial, int lane, int epi) {
   // rows of the MT m-tiles this lane loads (clamped: padding lanes re-read a valid row)
   int64_t arow[MT];
 #pragma unroll
@@ -111,10 +111,10 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
       f32x4v v = acc[j][t];
       if (partial != nullptr) {
         *reinterpret_cast<f32x4v*>(partial + (int64_t)(out_row0 + m) * P.N + n) = v;
-      } else if (P.epi == EPI_F32) {
+      } else if (epi == EPI_F32) {
         *reinterpret_cast<f32x4v*>(static_cast<float*>(P.C) + (int64_t)(out_row0 + m) * P.ldc + n) = v;
       } else {
-        if (P.epi == EPI_RELU2_BF16) {
+        if (epi == EPI_RELU2_BF16) {
           v[0] = relu2(v[0]); v[1] = relu2(v[1]); v[2] = relu2(v[2]); v[3] = relu2(v[3]);
         }
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)(out_row0 + m) * P.ldc + n) =
@@ -126,7 +126,10 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
 
 // One wavefront per (group, column block, k split); 4 waves per workgroup. A
 // column block is NSB slabs of 16 columns.
-template <int NSB>
+// GROUPED_EPI: -1 for dense products (epilogue from the problem), else the
+// fixed epilogue of a grouped expert product (which also names up and down
+// apart in profiles).
+template <int NSB, int GROUPED_EPI>
 __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -155,19 +158,20 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
   const int k_end = (int)((int64_t)ksteps * (ks + 1) / P.ksplit) * 32;
   float* partial = P.partial ? P.partial + (int64_t)ks * P.M * P.N : nullptr;
   const int n_first = blk * 16 * NSB;
+  const int epi = GROUPED_EPI >= 0 ? GROUPED_EPI : P.epi;
 
   // up to 64 rows in registers per pass; more rows take further passes
   for (int r0 = 0; r0 < rows; r0 += 64) {
     const int rr = min(64, rows - r0);
     if (rr <= 16)
       skinny_tile<1, NSB, 8 / NSB>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end, row0 + r0, partial,
-                                    lane);
+                                    lane, epi);
     else if (rr <= 32)
       skinny_tile<2, NSB, (4 / NSB > 0 ? 4 / NSB : 1)>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
-                                                        row0 + r0, partial, lane);
+                                                        row0 + r0, partial, lane, epi);
     else
       skinny_tile<4, NSB, (2 / NSB > 0 ? 2 / NSB : 1)>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
-                                                        row0 + r0, partial, lane);
+                                                        row0 + r0, partial, lane, epi);
   }
 }
 
@@ -199,8 +203,10 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
   const int64_t tasks = (int64_t)P.groups * nblocks * P.ksplit;
   if (tasks <= 0) return hipSuccess;
   const dim3 grid((unsigned)((tasks + 3) / 4)), block(256);
-  if (nsb == 4) hipLaunchKernelGGL(skinny_kernel<4>, grid, block, 0, st, P);
-  else hipLaunchKernelGGL(skinny_kernel<1>, grid, block, 0, st, P);
+  if (nsb == 4) hipLaunchKernelGGL((skinny_kernel<4, -1>), grid, block, 0, st, P);
+  else if (P.offsets == nullptr) hipLaunchKernelGGL((skinny_kernel<1, -1>), grid, block, 0, st, P);
+  else if (P.epi == EPI_RELU2_BF16) hipLaunchKernelGGL((skinny_kernel<1, EPI_RELU2_BF16>), grid, block, 0, st, P);
+  else hipLaunchKernelGGL((skinny_kernel<1, EPI_BF16>), grid, block, 0, st, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.partial == nullptr) return e;
   const int64_t total = (int64_t)P.M * P.N;

@@ -1,0 +1,124 @@
+"""Summaries of rocprofv3 runs of bench.py: kernel time tables and HBM traffic.
+
+    python -m sparse_moe_layer_correction_amd.profiling stats  STATS_CSV  OUT_MD  "COMMAND"
+    python -m sparse_moe_layer_correction_amd.profiling traffic WORKLOAD FETCH_CSV WRITE_CSV OUT_JSON "COMMANDS"
+
+``stats`` turns a ``rocprofv3 --kernel-trace --stats -f csv`` kernel_stats.csv
+into a short markdown table of the layer's kernels. ``traffic`` turns two
+``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` counter files of the same
+bench command into HBM bytes per launch for each phase of the forward, scaled
+by what the counters read for a plain device-to-device copy of known size that
+the same process ran (``bench.py --calibrate-copy``), and records them with a
+hash of the kernel source so that bench.py stops reporting them once the kernel
+changes.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sparse_moe_layer_correction_amd", "csrc")
+
+# kernel families and the sources that define them
+FAMILIES = {"gemm": ("gemm.h", "common.h"), "skinny": ("skinny.hip", "common.h")}
+
+# copy of known size made by bench.py --calibrate-copy (bytes read = bytes written)
+CALIBRATION_BYTES = 1 << 30
+
+
+def kernel_source_hash(family: str) -> str:
+    h = hashlib.sha256()
+    for f in FAMILIES[family]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    name = re.sub(r"\(.*$", "", name.replace("void ", ""))
+    return name.replace("moe::", "")
+
+
+def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    ours = [r for r in rows if "moe::" in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in ours)
+    lines = [f"# rocprofv3 kernel summary", "", "Command:", "", "```", command, "```", "",
+             "Kernels of the library only (the seeded input generator's torch kernels are left out).", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | total (ms) | share |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in sorted(ours, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(counter_csv: str, counter: str):
+    """[(kernel name, value in KiB)] in dispatch order."""
+    acc = defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        acc[d] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return [(names[d], acc[d]) for d in sorted(acc)]
+
+
+# which kernel a phase of the forward launches, by the order bench.py's profiled
+# step runs them (grouped launches carry their epilogue in the name)
+PHASE_KERNELS = {
+    "expert_up": (r"gemm_bf16_kernel<256, 256, 2, 4, 4, 1>", r"skinny_kernel<1, 1>"),
+    "expert_down": (r"gemm_bf16_kernel<256, 256, 2, 4, 4, 0>", r"skinny_kernel<1, 0>"),
+}
+
+
+def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, out_json: str, commands: str) -> dict:
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    cal_f = [v for n, v in fetch if "copyBuffer" in n or "copy" in n.lower()]
+    cal_w = [v for n, v in write if "copyBuffer" in n or "copy" in n.lower()]
+    if not cal_f or not cal_w:
+        raise SystemExit("no calibration copy found in the counter files")
+    # the largest copy is the calibration one
+    f_scale = CALIBRATION_BYTES / (max(cal_f) * 1024.0)
+    w_scale = CALIBRATION_BYTES / (max(cal_w) * 1024.0)
+    rec = {}
+    for phase, pats in PHASE_KERNELS.items():
+        for pat in pats:
+            fv = [v for n, v in fetch if pat in n]
+            wv = [v for n, v in write if pat in n]
+            if fv and wv:
+                family = "gemm" if "gemm" in pat else "skinny"
+                fb = sum(fv) / len(fv) * 1024.0 * f_scale
+                wb = sum(wv) / len(wv) * 1024.0 * w_scale
+                rec[phase] = {"kernel": pat, "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                              "bytes_per_launch": round(fb + wb), "launches": len(fv),
+                              "kernel_hash": kernel_source_hash(family)}
+    data = {}
+    if os.path.exists(out_json):
+        data = json.load(open(out_json))
+    data[workload] = {"phases": rec, "fetch_scale": f_scale, "write_scale": w_scale,
+                      "calibration": f"device-to-device copy of {CALIBRATION_BYTES} bytes",
+                      "commands": commands}
+    with open(out_json, "w") as f:
+        json.dump(data, f, indent=1)
+    return data
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "traffic":
+        print(json.dumps(summarize_traffic(*sys.argv[2:7]), indent=1))
+    else:
+        raise SystemExit(__doc__)
