@@ -74,7 +74,8 @@ typedef struct moe_weights {
 enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID = -1,      /* null pointer, non-positive size, K > E, bad C */
-  MOE_ERR_UNSUPPORTED = -2,  /* H, L, I or Is not a multiple of 64; E > 1024; K > 64 */
+  MOE_ERR_UNSUPPORTED = -2,  /* H, L, I or Is not a multiple of 64; E > 1024; K > 64;
+                                T*K >= 2^31; 2*T*L >= 2^32 */
   MOE_ERR_WORKSPACE = -3,    /* workspace null, too small or not 256-byte aligned */
   MOE_ERR_HIP = -4           /* a HIP launch failed */
 };

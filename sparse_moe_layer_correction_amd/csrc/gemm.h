@@ -11,19 +11,19 @@
 // router's three bf16 weight parts sum into one logit.
 //
 // Data movement (gfx950):
-//  * global -> LDS with global_load_lds_dwordx4 (16 bytes per lane, no VGPR
-//    staging) into a ring of STAGES separate LDS arrays, one per stage, so the
-//    compiler's alias analysis can tell the stage being read from the stages
-//    being filled and does not wait for every DMA in flight;
-//  * one k tile is 32 bf16 deep (64 bytes per row = 4 chunks of 16 bytes);
-//    chunk c of row r sits in slot c ^ ((r >> 2) & 3): gfx950's LDS serves a
-//    ds_read_b128 16 lanes per cycle over 64 banks, and the 16 rows those lanes
-//    read then fall into the 16 distinct 16-byte slots of a 256-byte window;
-//  * the DMA of each lane is chosen so that the 64 lanes of a wave fill 1 KB
-//    of LDS contiguously in that swizzled order (rows stay fully coalesced);
-//  * every step waits for its own tile (vmcnt), passes one barrier and issues
-//    the tile STAGES-1 ahead into the stage freed by the previous step; past
-//    the end it re-reads the last tile, so the wait count never changes.
+//  * global -> LDS by buffer loads that write LDS directly (16 bytes per lane,
+//    no VGPR staging), addressed through a buffer resource per operand with a
+//    fixed 32-bit offset per lane and the k position in the scalar offset;
+//  * one k tile is 64 bf16 deep, so each row contributes one whole 128-byte
+//    line per tile; chunk c of row r sits in slot c ^ ((r >> 1) & 7), which
+//    keeps the ds_read_b128 fragment reads free of bank conflicts on gfx950's
+//    64-bank LDS;
+//  * two LDS stages; per k tile, one barrier, placed so that the loads of the
+//    next-but-one tile and the first fragment reads of the next tile overlap
+//    the MFMAs of the current tile's last substep.
+// The 256x256 tile runs four waves of 128x128 each: a wave then reads half a
+// fragment per MFMA from LDS (a 128x64 wave tile reads three quarters), and
+// its 256 fp32 accumulators per lane live in AGPRs.
 // The MFMA is v_mfma_f32_32x32x16_bf16 with the B fragment as first operand,
 // so each lane owns 4 consecutive output columns of one output row.
 #pragma once
@@ -38,7 +38,7 @@ struct KSeg {
   const uint16_t* A;   // [rows, lda] bf16
   const uint16_t* B;   // [N, ldb] bf16 (expert 0's matrix in grouped mode)
   int64_t lda, ldb;
-  int K;               // multiple of 32
+  int K;               // multiple of 64
 };
 
 struct GemmProblem {
@@ -101,27 +101,60 @@ struct Stage {
   static constexpr int value = V;
 };
 
-// slot of logical chunk c of row r (4 chunks of 16 bytes per 64-byte row)
-__device__ __forceinline__ int swz_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
+// slot of logical chunk c of row r (8 chunks of 16 bytes per 128-byte row):
+// the 16 lanes a ds_read_b128 serves together read rows r0..r0+15 at one
+// logical chunk, and land in the 16 distinct slots of a 256-byte window.
+__device__ __forceinline__ int swz_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Buffer resource over [base, base + 4 GiB): raw (stride 0) descriptor, word 3
+// as the gfx9 family expects for untyped loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Stage<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Spread NDMA buffer loads and NREAD ds_reads over NMFMA MFMAs in the order the
+// scheduler emits them: per group, loads first, then a read, then MFMAs.
+template <int NMFMA, int NREAD, int NDMA>
+__device__ __forceinline__ void interleave() {
+  constexpr int G = NREAD > 0 ? NREAD : (NDMA > 0 ? NDMA : 1);
+  static_for<0, G>([&](auto gi) {
+    constexpr int g = decltype(gi)::value;
+    constexpr int nd = (g + 1) * NDMA / G - g * NDMA / G;
+    constexpr int nr = (g + 1) * NREAD / G - g * NREAD / G;
+    constexpr int nm = (g + 1) * NMFMA / G - g * NMFMA / G;
+    if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x020, nd, 0);
+    if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+    if constexpr (nm > 0) __builtin_amdgcn_sched_group_barrier(0x008, nm, 0);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // EPI: an Epilogue fixed at compile time, or -1 to take each problem's own.
-template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
-__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLaunch L) {
-  static_assert(STAGES >= 2 && STAGES <= 5, "stages");
-  constexpr int BK = 32, CPR = 4;
-  constexpr int NW = WM * WN;
+// OCC: waves per SIMD the register allocation is sized for (1 lets the 256x256
+// tile keep its 256 accumulators per lane in AGPRs next to 256 VGPRs).
+template <int BM, int BN, int WM, int WN, int EPI, int OCC>
+__global__ void __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+gemm_bf16_kernel(const GemmLaunch L) {
+  constexpr int BK = 64, CPR = 8;                  // k tile: 64 bf16 = 128 bytes per row
+  constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;      // wave tile
-  constexpr int TM = WTM / 32, TN = WTN / 32;      // MFMA tiles per wave
-  constexpr int NA = BM * CPR / (64 * NW);         // A DMA instructions per thread per k tile
-  constexpr int NB = BN * CPR / (64 * NW);
-  constexpr int PER_TILE = NA + NB;
+  constexpr int TM = WTM / 32, TN = WTN / 32;      // 32x32 MFMA tiles per wave
+  constexpr int NA = BM * CPR / NT;                // A loads per thread per k tile
+  constexpr int NB = BN * CPR / NT;
   constexpr int ACH = BM * CPR, BCH = BN * CPR;    // 16-byte chunks per stage
   static_assert(TM >= 1 && TN >= 1 && NA >= 1 && NB >= 1, "tile shape");
-  static_assert(NA * 64 * NW == ACH && NB * 64 * NW == BCH, "DMA coverage");
+  static_assert(NA * NT == ACH && NB * NT == BCH, "load coverage");
+  // two stages, each its own array so that the compiler can tell the stage
+  // being filled from the one being read
   __shared__ u32x4 sa0[ACH], sb0[BCH], sa1[ACH], sb1[BCH];
-  __shared__ u32x4 sa2[STAGES > 2 ? ACH : 1], sb2[STAGES > 2 ? BCH : 1];
-  __shared__ u32x4 sa3[STAGES > 3 ? ACH : 1], sb3[STAGES > 3 ? BCH : 1];
-  __shared__ u32x4 sa4[STAGES > 4 ? ACH : 1], sb4[STAGES > 4 ? BCH : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,57 +198,54 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
   }
   const int n0 = nt * BN;
 
-  // Rows and chunks this thread moves: DMA instruction i of wave w fills LDS
-  // chunks [(w*NA + i)*64, +64) of the A stage, lane l taking chunk position p.
-  int64_t arow[NA];
-  int acol[NA];
+  // Load i of a thread fills LDS chunks [(wave*NA + i)*64, +64) of the A stage
+  // (64 lanes x 16 bytes, contiguous), lane l taking chunk position p: row
+  // p / 8, slot p % 8, which holds logical chunk swz_slot(row, slot). Rows are
+  // taken relative to the tile's first row (gathered rows: absolute), so the
+  // 32-bit buffer offsets stay small; rows past the end repeat the last row.
+  int arow[NA], acol[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int p = (wave * NA + i) * 64 + lane;
     const int r = p / CPR;
     const int m = min(m0 + r, mend - 1);
-    arow[i] = P.gather ? (int64_t)P.gather[m] : (int64_t)m;
-    acol[i] = swz_slot(r, p % CPR) * 8;
+    arow[i] = P.gather ? P.gather[m] : m - m0;
+    acol[i] = swz_slot(r, p % CPR) * 16;
   }
   int brow[NB], bcol[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int p = (wave * NB + i) * 64 + lane;
     const int r = p / CPR;
-    brow[i] = min(n0 + r, P.Nb - 1);
-    bcol[i] = swz_slot(r, p % CPR) * 8;
+    brow[i] = min(n0 + r, P.Nb - 1) - n0;
+    bcol[i] = swz_slot(r, p % CPR) * 16;
   }
 
-  // K segments, walked by the DMA issue in increasing tile order.
+  // K segments, walked by the load issue in increasing k-tile order.
   int nk = 0;
   for (int s = 0; s < P.nseg; ++s) nk += P.seg[s].K / BK;
   int seg = 0, seg_k0 = 0, seg_end = P.seg[0].K / BK;
-  const uint16_t* ap[NA];
-  const uint16_t* bp[NB];
+  const uint16_t* abase;
+  const uint16_t* bbase;
+  uint32_t ao[NA], bo[NB];
   auto point = [&](int s) {
     const KSeg& S = P.seg[s];
+    abase = P.gather ? S.A : S.A + (int64_t)m0 * S.lda;
+    bbase = S.B + b_base + (int64_t)n0 * S.ldb;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) ap[i] = S.A + arow[i] * S.lda + acol[i];
+    for (int i = 0; i < NA; ++i) ao[i] = (uint32_t)((int64_t)arow[i] * S.lda * 2 + acol[i]);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) bp[i] = S.B + b_base + (int64_t)brow[i] * S.ldb + bcol[i];
+    for (int i = 0; i < NB; ++i) bo[i] = (uint32_t)((int64_t)brow[i] * S.ldb * 2 + bcol[i]);
   };
   point(0);
 
   auto stA = [&](auto st) -> u32x4* {
-    constexpr int v = decltype(st)::value;
-    if constexpr (v == 0) return sa0;
-    else if constexpr (v == 1) return sa1;
-    else if constexpr (v == 2) return sa2;
-    else if constexpr (v == 3) return sa3;
-    else return sa4;
+    if constexpr (decltype(st)::value == 0) return sa0;
+    else return sa1;
   };
   auto stB = [&](auto st) -> u32x4* {
-    constexpr int v = decltype(st)::value;
-    if constexpr (v == 0) return sb0;
-    else if constexpr (v == 1) return sb1;
-    else if constexpr (v == 2) return sb2;
-    else if constexpr (v == 3) return sb3;
-    else return sb4;
+    if constexpr (decltype(st)::value == 0) return sb0;
+    else return sb1;
   };
   auto issue = [&](int kt, auto st) {
     while (kt >= seg_end) {          // uniform; at most nseg-1 times in the whole loop
@@ -224,19 +254,40 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
       seg_end += P.seg[seg].K / BK;
       point(seg);
     }
-    const int koff = (kt - seg_k0) * BK;
+    const int so = (kt - seg_k0) * BK * 2;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(bbase);
+    // (the explicit casts of the lane offsets matter: without them the host
+    // pass silently drops this kernel's launch stub)
     u32x4* a = stA(st);
     u32x4* b = stB(st);
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(ap[i] + koff), (lds_void_ptr)&a[(wave * NA + i) * 64], 16,
-                                       0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)&a[(wave * NA + i) * 64], 16, (int)ao[i], so, 0, 0);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(bp[i] + koff), (lds_void_ptr)&b[(wave * NB + i) * 64], 16,
-                                       0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)&b[(wave * NB + i) * 64], 16, (int)bo[i], so, 0, 0);
   };
 
+  // Fragments of one 16-deep k substep: lane l reads row (l & 31) of each
+  // 32-row MFMA tile at logical chunk 2*ks + (l >> 5).
+  struct Frag {
+    bf16x8 a[TM], b[TN];
+  };
+  auto read = [&](Frag& f, auto st, int ks) {
+    const u32x4* a = stA(st);
+    const u32x4* b = stB(st);
+    const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int r = wave_m * WTM + tm * 32 + (lane & 31);
+      f.a[tm] = __builtin_bit_cast(bf16x8, a[r * CPR + swz_slot(r, ch)]);
+    }
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const int r = wave_n * WTN + tn * 32 + (lane & 31);
+      f.b[tn] = __builtin_bit_cast(bf16x8, b[r * CPR + swz_slot(r, ch)]);
+    }
+  };
   f32x16 acc[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
@@ -244,63 +295,53 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_kernel(const GemmLa
     for (int b = 0; b < TM; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.f;
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
+  };
 
+  // Step kt computes k tile kt from stage kt & 1 in four substeps; the reads of
+  // substep s+1 overlap the MFMAs of substep s. The one barrier sits before the
+  // last substep, whose fragments are then already in registers: past it, tile
+  // kt+1 has landed (every wave waited for its own loads) and nobody reads
+  // stage kt & 1 any more, so tile kt+2 is loaded into it while the last
+  // substep runs and the first fragments of tile kt+1 are read. Past the end
+  // the last tile is loaded again, so the schedule never changes.
+  constexpr int NM = TM * TN, NR = TM + TN;
+  Frag f0, f1;
   auto step = [&](int kt, auto st) {
     constexpr int S = decltype(st)::value;
-    MOE_WAIT_VMCNT((STAGES - 2) * PER_TILE);
-    // bare barrier: the wait above covers this wave's DMA of tile kt, the barrier
-    // everyone else's, and every wave is done with the stage refilled below
-    asm volatile("s_barrier" ::: "memory");
-    issue(min(kt + STAGES - 1, nk - 1), Stage<(S + STAGES - 1) % STAGES>{});
-    const u32x4* a = stA(st);
-    const u32x4* b = stB(st);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
-      bf16x8 af[TM], bf[TN];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int r = wave_m * WTM + tm * 32 + (lane & 31);
-        af[tm] = __builtin_bit_cast(bf16x8, a[r * CPR + swz_slot(r, ch)]);
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int r = wave_n * WTN + tn * 32 + (lane & 31);
-        bf[tn] = __builtin_bit_cast(bf16x8, b[r * CPR + swz_slot(r, ch)]);
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-          acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
-    }
+    read(f1, st, 1);
+    mma(f0);
+    interleave<NM, NR, 0>();
+    read(f0, st, 2);
+    mma(f1);
+    interleave<NM, NR, 0>();
+    read(f1, st, 3);
+    mma(f0);
+    interleave<NM, NR, 0>();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue(min(kt + 2, nk - 1), st);
+    read(f0, Stage<1 - S>{}, 0);
+    mma(f1);
+    interleave<NM, NR, NA + NB>();
   };
 
   issue(0, Stage<0>{});
-  if constexpr (STAGES > 2) issue(min(1, nk - 1), Stage<1>{});
-  if constexpr (STAGES > 3) issue(min(2, nk - 1), Stage<2>{});
-  if constexpr (STAGES > 4) issue(min(3, nk - 1), Stage<3>{});
-  // The unrolled body has no conditional steps (the compiler's wait analysis then
-  // sees the same DMA history on every trip); the remainder runs after it.
-  const int nfull = nk - nk % STAGES;
-  for (int kt = 0; kt < nfull; kt += STAGES) {
+  issue(min(1, nk - 1), Stage<1>{});
+  MOE_WAIT_VMCNT(NA + NB);
+  __syncthreads();
+  read(f0, Stage<0>{}, 0);
+  for (int kt = 0; kt + 1 < nk; kt += 2) {
     step(kt, Stage<0>{});
     step(kt + 1, Stage<1>{});
-    if constexpr (STAGES > 2) step(kt + 2, Stage<2>{});
-    if constexpr (STAGES > 3) step(kt + 3, Stage<3>{});
-    if constexpr (STAGES > 4) step(kt + 4, Stage<4>{});
   }
-  {
-    const int r = nk - nfull;
-    if (r > 0) step(nfull, Stage<0>{});
-    if constexpr (STAGES > 2)
-      if (r > 1) step(nfull + 1, Stage<1>{});
-    if constexpr (STAGES > 3)
-      if (r > 2) step(nfull + 2, Stage<2>{});
-    if constexpr (STAGES > 4)
-      if (r > 3) step(nfull + 3, Stage<3>{});
-  }
-  MOE_WAIT_VMCNT(0);   // no DMA may still be writing this workgroup's LDS when it ends
+  if (nk & 1) step(nk - 1, Stage<0>{});
+  MOE_WAIT_VMCNT(0);   // no load may still be writing this workgroup's LDS when it ends
 
   // Epilogue: lane owns row m = (lane & 31) of each MFMA tile and, for g = 0..3,
   // the four columns 8g + 4*(lane >> 5) + 0..3.

@@ -20,16 +20,16 @@ hipError_t launch_gemm(GemmLaunch& L, int cfg, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   const dim3 grid((unsigned)total);
   switch (cfg) {
-    case TILE_256x256: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, -1>), grid, dim3(512), 0, st, L); break;
-    case TILE_128x128: hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 4, -1>), grid, dim3(256), 0, st, L); break;
-    case TILE_64x256: hipLaunchKernelGGL((gemm_bf16_kernel<64, 256, 1, 4, 4, -1>), grid, dim3(256), 0, st, L); break;
+    case TILE_256x256: hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, -1, 1>), grid, dim3(256), 0, st, L); break;
+    case TILE_128x128: hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, -1, 2>), grid, dim3(256), 0, st, L); break;
+    case TILE_64x256: hipLaunchKernelGGL((gemm_bf16_kernel<64, 256, 1, 4, -1, 2>), grid, dim3(256), 0, st, L); break;
     // grouped expert products: one problem, epilogue fixed at compile time (the
     // up and down products are then also told apart by name in profiles)
     case TILE_256x256_GROUPED:
       if (L.p[0].epi == EPI_RELU2_BF16)
-        hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, EPI_RELU2_BF16>), grid, dim3(512), 0, st, L);
+        hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, EPI_RELU2_BF16, 1>), grid, dim3(256), 0, st, L);
       else
-        hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, EPI_BF16>), grid, dim3(512), 0, st, L);
+        hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, EPI_BF16, 1>), grid, dim3(256), 0, st, L);
       break;
     default: return hipErrorInvalidValue;
   }

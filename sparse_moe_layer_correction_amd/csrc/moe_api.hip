@@ -66,6 +66,8 @@ bool dims_ok(const moe_dims* d, int* status, int use = USE_ALL) {
   // permuted rows are indexed with int32; byte offsets of one tensor stay below 2^40
   const int64_t tk = (int64_t)d->T * d->K;
   if (tk > (int64_t)0x7FFFFFFF) return false;
+  // the expert up product gathers rows of z [T, L] through 32-bit byte offsets
+  if (use == USE_ALL && (int64_t)d->T * d->L * 2 >= ((int64_t)1 << 32)) return false;
   *status = MOE_OK;
   return true;
 }
@@ -258,7 +260,8 @@ const char* moe_status_string(int status) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID: return "invalid argument (null pointer, non-positive size, K > E or bad row length)";
     case MOE_ERR_UNSUPPORTED:
-      return "unsupported size (H, L, I, Is must be multiples of 64; E <= 1024; K <= 64; T*K < 2^31)";
+      return "unsupported size (H, L, I, Is must be multiples of 64; E <= 1024; K <= 64; T*K < 2^31; "
+             "2*T*L < 2^32)";
     case MOE_ERR_WORKSPACE: return "workspace null, too small or not 256-byte aligned";
     case MOE_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
