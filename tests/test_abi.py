@@ -96,6 +96,8 @@ def test_workspace_sizes_at_every_token_count(lib, T):
     (dict(T=0), -1), (dict(K=0), -1), (dict(K=17), -1), (dict(H=-64), -1),
     (dict(H=100), -2), (dict(L=96), -2), (dict(I=1000), -2), (dict(Is=65), -2),
     (dict(E=2048, K=4), -2), (dict(K=65, E=100), -2),
+    # gathered latent rows are addressed with 32-bit byte offsets: 2*T*L < 2^32
+    (dict(T=1 << 20, L=2048), -2), (dict(T=1 << 28, K=8), -2),
 ])
 def test_forward_rejects_bad_dims(lib, bad, code):
     base = dict(T=TINY.T, H=TINY.H, L=TINY.L, E=TINY.E, I=TINY.I, K=TINY.K, Is=TINY.Is)
