@@ -127,6 +127,8 @@ def main():
 
     offsets = ws[lay["offsets"]:lay["offsets"] + 4 * (cfg.E + 1)].view(torch.int32).cpu().numpy()
     n_touched = int(np.count_nonzero(np.diff(offsets)))
+    # rows the grouped 256-row tiles cover (each expert's tail tile is padded)
+    m_tiles = int(np.sum((np.diff(offsets) + 255) // 256))
     idx_gpu = ws[lay["idx"]:lay["idx"] + 4 * cfg.T * cfg.K].view(torch.int32).view(cfg.T, cfg.K).cpu().numpy()
     flops, bytes_ = phase_work(cfg, n_touched)
     total_flops = sum(flops.values())
@@ -181,6 +183,8 @@ def main():
         "hbm_gbs_layer": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "hbm_frac_layer": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "experts_touched": n_touched,
+        "grouped_m_tiles": m_tiles,
+        "grouped_row_padding": round(1 - cfg.T * cfg.K / max(1, m_tiles * 256), 4),
         "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "events_ms_per_step": round(ev_ms, 4),
         "roofline": roofline,

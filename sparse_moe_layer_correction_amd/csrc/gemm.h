@@ -183,194 +183,213 @@ gemm_bf16_kernel(const GemmLaunch L) {
     if (L.np > 1 && bid >= L.tiles0) { pi = 1; bid -= L.tiles0; }
     tile_order(bid, L.p[pi].mtiles, L.p[pi].ntiles, L.p[pi].group_m, mt, nt);
   }
-  const GemmProblem& P = L.p[pi];
+  const GemmProblem& Q = L.p[pi];
 
   int m0, mend;
   int64_t b_base = 0;
-  if (P.tile_e != nullptr) {
-    const int e = P.tile_e[mt];
-    m0 = P.tile_m0[mt];
-    mend = P.offsets[e + 1];
-    b_base = (int64_t)e * P.b_estride;
+  if (Q.tile_e != nullptr) {
+    const int e = Q.tile_e[mt];
+    m0 = Q.tile_m0[mt];
+    mend = Q.offsets[e + 1];
+    b_base = (int64_t)e * Q.b_estride;
   } else {
     m0 = mt * BM;
-    mend = P.M;
+    mend = Q.M;
   }
   const int n0 = nt * BN;
 
-  // Load i of a thread fills LDS chunks [(wave*NA + i)*64, +64) of the A stage
-  // (64 lanes x 16 bytes, contiguous), lane l taking chunk position p: row
-  // p / 8, slot p % 8, which holds logical chunk swz_slot(row, slot). Rows are
-  // taken relative to the tile's first row (gathered rows: absolute), so the
-  // 32-bit buffer offsets stay small; rows past the end repeat the last row.
-  int arow[NA], acol[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int p = (wave * NA + i) * 64 + lane;
-    const int r = p / CPR;
-    const int m = min(m0 + r, mend - 1);
-    arow[i] = P.gather ? P.gather[m] : m - m0;
-    acol[i] = swz_slot(r, p % CPR) * 16;
-  }
-  int brow[NB], bcol[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int p = (wave * NB + i) * 64 + lane;
-    const int r = p / CPR;
-    brow[i] = min(n0 + r, P.Nb - 1) - n0;
-    bcol[i] = swz_slot(r, p % CPR) * 16;
-  }
-
-  // K segments, walked by the load issue in increasing k-tile order.
-  int nk = 0;
-  for (int s = 0; s < P.nseg; ++s) nk += P.seg[s].K / BK;
-  int seg = 0, seg_k0 = 0, seg_end = P.seg[0].K / BK;
-  const uint16_t* abase;
-  const uint16_t* bbase;
-  uint32_t ao[NA], bo[NB];
-  auto point = [&](int s) {
-    const KSeg& S = P.seg[s];
-    abase = P.gather ? S.A : S.A + (int64_t)m0 * S.lda;
-    bbase = S.B + b_base + (int64_t)n0 * S.ldb;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) ao[i] = (uint32_t)((int64_t)arow[i] * S.lda * 2 + acol[i]);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) bo[i] = (uint32_t)((int64_t)brow[i] * S.ldb * 2 + bcol[i]);
-  };
-  point(0);
-
-  auto stA = [&](auto st) -> u32x4* {
-    if constexpr (decltype(st)::value == 0) return sa0;
-    else return sa1;
-  };
-  auto stB = [&](auto st) -> u32x4* {
-    if constexpr (decltype(st)::value == 0) return sb0;
-    else return sb1;
-  };
-  auto issue = [&](int kt, auto st) {
-    while (kt >= seg_end) {          // uniform; at most nseg-1 times in the whole loop
-      seg_k0 = seg_end;
-      ++seg;
-      seg_end += P.seg[seg].K / BK;
-      point(seg);
+  // In the grouped products (the instantiations with a fixed epilogue), an
+  // expert's tail tile with at most BM/2 valid rows runs the half path: the same
+  // waves split BM/2 rows, so it costs about half a full tile instead of a full
+  // one (the tail tiles are about a sixth of the padded rows at 704 rows per
+  // expert).
+  constexpr bool kHalfTiles = BM == 256 && WM == 2 && EPI >= 0;
+  auto body = [&](const GemmProblem& P, auto mode) __attribute__((always_inline)) {
+    constexpr bool HALF = decltype(mode)::value == 1;
+    constexpr int NAX = HALF ? NA / 2 : NA;        // A loads per thread per k tile
+    constexpr int TMX = HALF ? TM / 2 : TM;        // 32-row MFMA tiles per wave
+    constexpr int WTMX = HALF ? WTM / 2 : WTM;     // wave tile rows
+    // Load i of a thread fills LDS chunks [(wave*NAX + i)*64, +64) of the A stage
+    // (64 lanes x 16 bytes, contiguous), lane l taking chunk position p: row
+    // p / 8, slot p % 8, which holds logical chunk swz_slot(row, slot). Rows are
+    // taken relative to the tile's first row (gathered rows: absolute), so the
+    // 32-bit buffer offsets stay small; rows past the end repeat the last row.
+    int arow[NAX], acol[NAX];
+  #pragma unroll
+    for (int i = 0; i < NAX; ++i) {
+      const int p = (wave * NAX + i) * 64 + lane;
+      const int r = p / CPR;
+      const int m = min(m0 + r, mend - 1);
+      arow[i] = P.gather ? P.gather[m] : m - m0;
+      acol[i] = swz_slot(r, p % CPR) * 16;
     }
-    const int so = (kt - seg_k0) * BK * 2;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(bbase);
-    // (the explicit casts of the lane offsets matter: without them the host
-    // pass silently drops this kernel's launch stub)
-    u32x4* a = stA(st);
-    u32x4* b = stB(st);
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)&a[(wave * NA + i) * 64], 16, (int)ao[i], so, 0, 0);
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)&b[(wave * NB + i) * 64], 16, (int)bo[i], so, 0, 0);
-  };
-
-  // Fragments of one 16-deep k substep: lane l reads row (l & 31) of each
-  // 32-row MFMA tile at logical chunk 2*ks + (l >> 5).
-  struct Frag {
-    bf16x8 a[TM], b[TN];
-  };
-  auto read = [&](Frag& f, auto st, int ks) {
-    const u32x4* a = stA(st);
-    const u32x4* b = stB(st);
-    const int ch = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int r = wave_m * WTM + tm * 32 + (lane & 31);
-      f.a[tm] = __builtin_bit_cast(bf16x8, a[r * CPR + swz_slot(r, ch)]);
+    int brow[NB], bcol[NB];
+  #pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int p = (wave * NB + i) * 64 + lane;
+      const int r = p / CPR;
+      brow[i] = min(n0 + r, P.Nb - 1) - n0;
+      bcol[i] = swz_slot(r, p % CPR) * 16;
     }
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const int r = wave_n * WTN + tn * 32 + (lane & 31);
-      f.b[tn] = __builtin_bit_cast(bf16x8, b[r * CPR + swz_slot(r, ch)]);
+
+    // K segments, walked by the load issue in increasing k-tile order.
+    int nk = 0;
+    for (int s = 0; s < P.nseg; ++s) nk += P.seg[s].K / BK;
+    int seg = 0, seg_k0 = 0, seg_end = P.seg[0].K / BK;
+    const uint16_t* abase;
+    const uint16_t* bbase;
+    uint32_t ao[NAX], bo[NB];
+    auto point = [&](int s) {
+      const KSeg& S = P.seg[s];
+      abase = P.gather ? S.A : S.A + (int64_t)m0 * S.lda;
+      bbase = S.B + b_base + (int64_t)n0 * S.ldb;
+  #pragma unroll
+      for (int i = 0; i < NAX; ++i) ao[i] = (uint32_t)((int64_t)arow[i] * S.lda * 2 + acol[i]);
+  #pragma unroll
+      for (int i = 0; i < NB; ++i) bo[i] = (uint32_t)((int64_t)brow[i] * S.ldb * 2 + bcol[i]);
+    };
+    point(0);
+
+    auto stA = [&](auto st) -> u32x4* {
+      if constexpr (decltype(st)::value == 0) return sa0;
+      else return sa1;
+    };
+    auto stB = [&](auto st) -> u32x4* {
+      if constexpr (decltype(st)::value == 0) return sb0;
+      else return sb1;
+    };
+    auto issue = [&](int kt, auto st) {
+      while (kt >= seg_end) {          // uniform; at most nseg-1 times in the whole loop
+        seg_k0 = seg_end;
+        ++seg;
+        seg_end += P.seg[seg].K / BK;
+        point(seg);
+      }
+      const int so = (kt - seg_k0) * BK * 2;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(bbase);
+      // (the explicit casts of the lane offsets matter: without them the host
+      // pass silently drops this kernel's launch stub)
+      u32x4* a = stA(st);
+      u32x4* b = stB(st);
+  #pragma unroll
+      for (int i = 0; i < NAX; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)&a[(wave * NAX + i) * 64], 16, (int)ao[i], so, 0, 0);
+  #pragma unroll
+      for (int i = 0; i < NB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)&b[(wave * NB + i) * 64], 16, (int)bo[i], so, 0, 0);
+    };
+
+    // Fragments of one 16-deep k substep: lane l reads row (l & 31) of each
+    // 32-row MFMA tile at logical chunk 2*ks + (l >> 5).
+    struct Frag {
+      bf16x8 a[TMX], b[TN];
+    };
+    auto read = [&](Frag& f, auto st, int ks) {
+      const u32x4* a = stA(st);
+      const u32x4* b = stB(st);
+      const int ch = ks * 2 + (lane >> 5);
+  #pragma unroll
+      for (int tm = 0; tm < TMX; ++tm) {
+        const int r = wave_m * WTMX + tm * 32 + (lane & 31);
+        f.a[tm] = __builtin_bit_cast(bf16x8, a[r * CPR + swz_slot(r, ch)]);
+      }
+  #pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int r = wave_n * WTN + tn * 32 + (lane & 31);
+        f.b[tn] = __builtin_bit_cast(bf16x8, b[r * CPR + swz_slot(r, ch)]);
+      }
+    };
+    f32x16 acc[TN][TMX];
+  #pragma unroll
+    for (int a = 0; a < TN; ++a)
+  #pragma unroll
+      for (int b = 0; b < TMX; ++b)
+  #pragma unroll
+        for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.f;
+    auto mma = [&](const Frag& f) {
+  #pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+  #pragma unroll
+        for (int tm = 0; tm < TMX; ++tm)
+          acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
+    };
+
+    // Step kt computes k tile kt from stage kt & 1 in four substeps; the reads of
+    // substep s+1 overlap the MFMAs of substep s. The one barrier sits before the
+    // last substep, whose fragments are then already in registers: past it, tile
+    // kt+1 has landed (every wave waited for its own loads) and nobody reads
+    // stage kt & 1 any more, so tile kt+2 is loaded into it while the last
+    // substep runs and the first fragments of tile kt+1 are read. Past the end
+    // the last tile is loaded again, so the schedule never changes.
+    constexpr int NM = TMX * TN, NR = TMX + TN;
+    Frag f0, f1;
+    auto step = [&](int kt, auto st) {
+      constexpr int S = decltype(st)::value;
+      read(f1, st, 1);
+      mma(f0);
+      interleave<NM, NR, 0>();
+      read(f0, st, 2);
+      mma(f1);
+      interleave<NM, NR, 0>();
+      read(f1, st, 3);
+      mma(f0);
+      interleave<NM, NR, 0>();
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(kt + 2, nk - 1), st);
+      read(f0, Stage<1 - S>{}, 0);
+      mma(f1);
+      interleave<NM, NR, NAX + NB>();
+    };
+
+    issue(0, Stage<0>{});
+    issue(min(1, nk - 1), Stage<1>{});
+    MOE_WAIT_VMCNT(NAX + NB);
+    __syncthreads();
+    read(f0, Stage<0>{}, 0);
+    for (int kt = 0; kt + 1 < nk; kt += 2) {
+      step(kt, Stage<0>{});
+      step(kt + 1, Stage<1>{});
     }
-  };
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.f;
-  auto mma = [&](const Frag& f) {
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-        acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[tn], f.a[tm], acc[tn][tm], 0, 0, 0);
-  };
+    if (nk & 1) step(nk - 1, Stage<0>{});
+    MOE_WAIT_VMCNT(0);   // no load may still be writing this workgroup's LDS when it ends
 
-  // Step kt computes k tile kt from stage kt & 1 in four substeps; the reads of
-  // substep s+1 overlap the MFMAs of substep s. The one barrier sits before the
-  // last substep, whose fragments are then already in registers: past it, tile
-  // kt+1 has landed (every wave waited for its own loads) and nobody reads
-  // stage kt & 1 any more, so tile kt+2 is loaded into it while the last
-  // substep runs and the first fragments of tile kt+1 are read. Past the end
-  // the last tile is loaded again, so the schedule never changes.
-  constexpr int NM = TM * TN, NR = TM + TN;
-  Frag f0, f1;
-  auto step = [&](int kt, auto st) {
-    constexpr int S = decltype(st)::value;
-    read(f1, st, 1);
-    mma(f0);
-    interleave<NM, NR, 0>();
-    read(f0, st, 2);
-    mma(f1);
-    interleave<NM, NR, 0>();
-    read(f1, st, 3);
-    mma(f0);
-    interleave<NM, NR, 0>();
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    issue(min(kt + 2, nk - 1), st);
-    read(f0, Stage<1 - S>{}, 0);
-    mma(f1);
-    interleave<NM, NR, NA + NB>();
-  };
-
-  issue(0, Stage<0>{});
-  issue(min(1, nk - 1), Stage<1>{});
-  MOE_WAIT_VMCNT(NA + NB);
-  __syncthreads();
-  read(f0, Stage<0>{}, 0);
-  for (int kt = 0; kt + 1 < nk; kt += 2) {
-    step(kt, Stage<0>{});
-    step(kt + 1, Stage<1>{});
-  }
-  if (nk & 1) step(nk - 1, Stage<0>{});
-  MOE_WAIT_VMCNT(0);   // no load may still be writing this workgroup's LDS when it ends
-
-  // Epilogue: lane owns row m = (lane & 31) of each MFMA tile and, for g = 0..3,
-  // the four columns 8g + 4*(lane >> 5) + 0..3.
-  const int epi = EPI >= 0 ? EPI : P.epi;
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int m = m0 + wave_m * WTM + tm * 32 + (lane & 31);
-    if (m >= mend) continue;
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wave_n * WTN + tn * 32 + 8 * g + 4 * (lane >> 5);
-        if (n >= P.N) continue;
-        float v0 = acc[tn][tm][4 * g + 0], v1 = acc[tn][tm][4 * g + 1];
-        float v2 = acc[tn][tm][4 * g + 2], v3 = acc[tn][tm][4 * g + 3];
-        if (epi == EPI_F32) {
-          f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(P.C) + (int64_t)m * P.ldc + n);
-          *dst = f32x4{v0, v1, v2, v3};
-        } else {
-          if (epi == EPI_RELU2_BF16) {
-            v0 = relu2(v0); v1 = relu2(v1); v2 = relu2(v2); v3 = relu2(v3);
+    // Epilogue: lane owns row m = (lane & 31) of each MFMA tile and, for g = 0..3,
+    // the four columns 8g + 4*(lane >> 5) + 0..3.
+    const int epi = EPI >= 0 ? EPI : P.epi;
+  #pragma unroll
+    for (int tm = 0; tm < TMX; ++tm) {
+      const int m = m0 + wave_m * WTMX + tm * 32 + (lane & 31);
+      if (m >= mend) continue;
+  #pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wave_n * WTN + tn * 32 + 8 * g + 4 * (lane >> 5);
+          if (n >= P.N) continue;
+          float v0 = acc[tn][tm][4 * g + 0], v1 = acc[tn][tm][4 * g + 1];
+          float v2 = acc[tn][tm][4 * g + 2], v3 = acc[tn][tm][4 * g + 3];
+          if (epi == EPI_F32) {
+            f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(P.C) + (int64_t)m * P.ldc + n);
+            *dst = f32x4{v0, v1, v2, v3};
+          } else {
+            if (epi == EPI_RELU2_BF16) {
+              v0 = relu2(v0); v1 = relu2(v1); v2 = relu2(v2); v3 = relu2(v3);
+            }
+            u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n);
+            *dst = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
           }
-          u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n);
-          *dst = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
       }
     }
+  };
+  if constexpr (kHalfTiles) {
+    if (mend - m0 <= BM / 2) {
+      body(L.p[0], Stage<1>{});
+      return;
+    }
   }
+  body(L.p[pi], Stage<0>{});
 }
 
 }  // namespace moe
