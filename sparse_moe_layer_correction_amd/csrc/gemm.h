@@ -106,6 +106,13 @@ struct Stage {
 // logical chunk, and land in the 16 distinct slots of a 256-byte window.
 __device__ __forceinline__ int swz_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+// two fp32 -> packed bf16x2, round to nearest even (one v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2_t));
+}
+
 // Buffer resource over [base, base + 4 GiB): raw (stride 0) descriptor, word 3
 // as the gfx9 family expects for untyped loads.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
@@ -354,33 +361,68 @@ gemm_bf16_kernel(const GemmLaunch L) {
     if (nk & 1) step(nk - 1, Stage<0>{});
     MOE_WAIT_VMCNT(0);   // no load may still be writing this workgroup's LDS when it ends
 
-    // Epilogue: lane owns row m = (lane & 31) of each MFMA tile and, for g = 0..3,
-    // the four columns 8g + 4*(lane >> 5) + 0..3.
+    // Epilogue. Lane l owns row (l & 31) of each 32x32 MFMA tile and, for
+    // g = 0..3, the four columns 8g + 4*(l >> 5) + 0..3.
     const int epi = EPI >= 0 ? EPI : P.epi;
-  #pragma unroll
+    if (EPI < 0 && epi == EPI_F32) {
+      // fp32 results (router logits): straight from the accumulators
+#pragma unroll
+      for (int tm = 0; tm < TMX; ++tm) {
+        const int m = m0 + wave_m * WTMX + tm * 32 + (lane & 31);
+        if (m >= mend) continue;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wave_n * WTN + tn * 32 + 8 * g + 4 * (lane >> 5);
+            if (n >= P.N) continue;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(P.C) + (int64_t)m * P.ldc + n) =
+                f32x4{acc[tn][tm][4 * g], acc[tn][tm][4 * g + 1], acc[tn][tm][4 * g + 2], acc[tn][tm][4 * g + 3]};
+          }
+      }
+      return;
+    }
+    // bf16 results go through LDS, so that every store writes whole rows of
+    // the wave tile (WTN * 2 bytes) instead of 16-byte pieces of 32 rows. Each
+    // wave stages its tile in one of the (now idle) stage arrays, 16-byte chunk
+    // c of tile row r at chunk c ^ (r % CPW): the 32 rows a ds_write_b64 hits
+    // then fall on distinct banks pairwise, and a row reads back contiguously.
+    constexpr int CPW = WTN / 8;                   // 16-byte chunks per wave-tile row
+    static_assert(WTMX * WTN * 2 <= ACH * 16 && WTMX * WTN * 2 <= BCH * 16, "staging fits a stage array");
+    MOE_WAIT_VMCNT(0);
+    __syncthreads();                               // all loads landed, all fragment reads done
+    char* stg = reinterpret_cast<char*>(wave == 0 ? sa0 : wave == 1 ? sb0 : wave == 2 ? sa1 : sb1);
+    const bool r2 = epi == EPI_RELU2_BF16;
+#pragma unroll
     for (int tm = 0; tm < TMX; ++tm) {
-      const int m = m0 + wave_m * WTMX + tm * 32 + (lane & 31);
-      if (m >= mend) continue;
-  #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-  #pragma unroll
+      const int r = tm * 32 + (lane & 31);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wave_n * WTN + tn * 32 + 8 * g + 4 * (lane >> 5);
-          if (n >= P.N) continue;
           float v0 = acc[tn][tm][4 * g + 0], v1 = acc[tn][tm][4 * g + 1];
           float v2 = acc[tn][tm][4 * g + 2], v3 = acc[tn][tm][4 * g + 3];
-          if (epi == EPI_F32) {
-            f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(P.C) + (int64_t)m * P.ldc + n);
-            *dst = f32x4{v0, v1, v2, v3};
-          } else {
-            if (epi == EPI_RELU2_BF16) {
-              v0 = relu2(v0); v1 = relu2(v1); v2 = relu2(v2); v3 = relu2(v3);
-            }
-            u32x2* dst = reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n);
-            *dst = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          if (r2) {
+            v0 = relu2(v0); v1 = relu2(v1); v2 = relu2(v2); v3 = relu2(v3);
           }
+          const int c = tn * 4 + g;
+          *reinterpret_cast<u32x2*>(stg + r * (CPW * 16) + ((c ^ (r % CPW)) * 16) + (lane >> 5) * 8) =
+              u32x2{cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3)};
         }
-      }
+    }
+    // read back: 64 / CPW rows per instruction, CPW lanes per row
+    constexpr int RPI = 64 / CPW;
+#pragma unroll
+    for (int i = 0; i < WTMX / RPI; ++i) {
+      const int r = i * RPI + lane / CPW;
+      const int c = lane % CPW;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (CPW * 16) + ((c ^ (r % CPW)) * 16));
+      const int m = m0 + wave_m * WTMX + r;
+      const int n = n0 + wave_n * WTN + c * 8;
+      if (m >= mend || n >= P.N) continue;
+      uint16_t* dst = static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n;
+      if (n + 8 <= P.N) *reinterpret_cast<u32x4*>(dst) = v;
+      else *reinterpret_cast<u32x2*>(dst) = u32x2{v[0], v[1]};   // N is a multiple of 4
     }
   };
   if constexpr (kHalfTiles) {
