@@ -115,8 +115,10 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 
 // Buffer resource over [base, base + 4 GiB): raw (stride 0) descriptor, word 3
 // as the gfx9 family expects for untyped loads.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+// num_records 0 makes every lane out of range: the load then touches no memory
+// (buffer range checking returns zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_records = 0x7FFFFFFF) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, 0x00020000);
 }
 
 template <int I, int N, typename F>
@@ -265,7 +267,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
       if constexpr (decltype(st)::value == 0) return sb0;
       else return sb1;
     };
-    auto issue = [&](int kt, auto st) {
+    auto issue = [&](int kt, auto st, bool live = true) {
       while (kt >= seg_end) {          // uniform; at most nseg-1 times in the whole loop
         seg_k0 = seg_end;
         ++seg;
@@ -273,7 +275,8 @@ gemm_bf16_kernel(const GemmLaunch L) {
         point(seg);
       }
       const int so = (kt - seg_k0) * BK * 2;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase), rb = make_rsrc(bbase);
+      const int nrec = live ? 0x7FFFFFFF : 0;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, nrec), rb = make_rsrc(bbase, nrec);
       // (the explicit casts of the lane offsets matter: without them the host
       // pass silently drops this kernel's launch stub)
       u32x4* a = stA(st);
@@ -326,8 +329,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
     // last substep, whose fragments are then already in registers: past it, tile
     // kt+1 has landed (every wave waited for its own loads) and nobody reads
     // stage kt & 1 any more, so tile kt+2 is loaded into it while the last
-    // substep runs and the first fragments of tile kt+1 are read. Past the end
-    // the last tile is loaded again, so the schedule never changes.
+    // substep runs and the first fragments of tile kt+1 are read.
     constexpr int NM = TMX * TN, NR = TMX + TN;
     Frag f0, f1;
     auto step = [&](int kt, auto st) {
@@ -343,7 +345,9 @@ gemm_bf16_kernel(const GemmLaunch L) {
       interleave<NM, NR, 0>();
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      issue(min(kt + 2, nk - 1), st);
+      // past the end the load still runs (the schedule stays the same) but over
+      // an empty range, so it moves no data and lands at once
+      issue(min(kt + 2, nk - 1), st, kt + 2 < nk);
       read(f0, Stage<1 - S>{}, 0);
       mma(f1);
       interleave<NM, NR, NAX + NB>();
