@@ -24,7 +24,14 @@ with
 
 Readings where the pages leave a step open (each listed in the design notes):
   * the router reads the uncompressed x (QA Q5.2 flattens to hidden_size);
-  * one expert group: top-K over all E experts;
+  * expert groups: WT "路由与共享专家" says the top-K is taken within groups,
+    and QA CH9 Q9.2 has the MoE inherit DeepseekV3MoE's routing, but no page
+    gives a group count or the group rule. ``route`` takes n_group /
+    topk_group (default 1 / 1: top-K over all E experts) and follows the
+    DeepSeek-V3 rule of that parent: experts form n_group equal contiguous
+    groups, a group scores the sum of its two highest choice scores (of its
+    one score if it has one expert), the topk_group best groups (ties: lower
+    group index) admit their experts, and the top-K is taken among those;
   * dropless: every (token, expert) pair is computed;
   * ties in the choice score go to the lower expert index;
   * a token's K experts are reported in ascending expert order (the sum over
@@ -89,10 +96,17 @@ class RouteResult:
 
 
 def route(x: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray, K: int,
-          routed_scaling: float) -> RouteResult:
+          routed_scaling: float, n_group: int = 1, topk_group: int = 1) -> RouteResult:
     """Router of QA Q5.2 / Q5.3 with the gate rule of WT "路由与共享专家" and QA Q5.8.
 
     x: [T,H] float64 (bf16 values); w_router: [E,H] (fp32 values); corr_bias: [E].
+    n_group / topk_group: group-limited selection (module docstring); 1 / 1 is
+    the plain top-K over all experts.
+
+    gap[t] is the smallest margin that decides token t's routing: the K-th
+    minus the (K+1)-th choice score among the admitted experts, and, with
+    groups, the topk_group-th minus the next group score (inf when nothing
+    follows).
     """
     x = np.asarray(x, dtype=np.float64)
     wr = np.asarray(w_router, dtype=np.float64)
@@ -100,18 +114,28 @@ def route(x: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray, K: int,
     T = x.shape[0]
     E = wr.shape[0]
     assert np.all(np.isfinite(x)) and np.all(np.isfinite(wr)) and np.all(np.isfinite(b))
-    assert 1 <= K <= E
+    assert n_group >= 1 and E % n_group == 0 and 1 <= topk_group <= n_group
+    G = E // n_group
+    assert 1 <= K <= topk_group * G
     logits = x @ wr.T                                  # fp32 inputs, exact products in fp64
     score = 1.0 / (1.0 + np.exp(-logits))              # independent per expert (QA Q5.2)
     choice = score + b[None, :]                        # bias steers the choice only (QA Q5.3)
     experts = np.arange(E)
+    groups = np.arange(n_group)
     idx = np.empty((T, K), dtype=np.int32)
     gap = np.empty(T, dtype=np.float64)
     for t in range(T):
+        c = choice[t]
+        # group score: the sum of the group's two highest choice scores
+        gs = np.array([np.sort(c[g * G:(g + 1) * G])[::-1][:2].sum() for g in groups])
+        gorder = np.lexsort((groups, -gs))             # best groups first, ties -> lower group
+        admitted = np.sort(np.concatenate([experts[g * G:(g + 1) * G] for g in gorder[:topk_group]]))
         # descending choice score, equal scores -> lower expert index first
-        order = np.lexsort((experts, -choice[t]))
+        order = admitted[np.lexsort((admitted, -c[admitted]))]
         chosen = order[:K]
-        gap[t] = choice[t, order[K - 1]] - choice[t, order[K]] if K < E else np.inf
+        egap = c[order[K - 1]] - c[order[K]] if K < len(order) else np.inf
+        ggap = gs[gorder[topk_group - 1]] - gs[gorder[topk_group]] if topk_group < n_group else np.inf
+        gap[t] = min(egap, ggap)
         idx[t] = np.sort(chosen)
     s_sel = np.take_along_axis(score, idx.astype(np.int64), axis=1)
     gate = (routed_scaling * s_sel / s_sel.sum(axis=1, keepdims=True)).astype(np.float32)
@@ -179,7 +203,7 @@ def forward(x_bits: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray,
             expert: Callable[[int], Tuple[np.ndarray, np.ndarray]],
             K: int, routed_scaling: float, mirror: bool = True,
             idx_override: Optional[np.ndarray] = None,
-            keep: bool = False) -> Dict[str, np.ndarray]:
+            keep: bool = False, n_group: int = 1, topk_group: int = 1) -> Dict[str, np.ndarray]:
     """One forward of the layer on the tokens in ``x_bits`` (tokens are independent).
 
     x_bits [T,H] and the *_bits weights are bf16 bit patterns (uint16);
@@ -198,7 +222,7 @@ def forward(x_bits: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray,
     x = bf16_bits_to_f64(x_bits)
     T, H = x.shape
     E = np.asarray(w_router).shape[0]
-    r = route(x, w_router, corr_bias, K, routed_scaling)
+    r = route(x, w_router, corr_bias, K, routed_scaling, n_group, topk_group)
     if idx_override is not None:
         idx = np.sort(np.asarray(idx_override, dtype=np.int64), axis=1).astype(np.int32)
         assert idx.shape == (T, K)

@@ -174,6 +174,84 @@ def pin_route_ties(O):
 
 
 # ----------------------------------------------------------------------------
+# group-limited router (n_group equal contiguous groups, group score = sum of
+# the group's two highest choice scores, topk_group groups admitted)
+# ----------------------------------------------------------------------------
+
+def _group_brute(ch_t, E, K, n_group, topk_group):
+    """Expected (set, gap) for one token by plain Python ranking and subset enumeration."""
+    G = E // n_group
+    gs = [sum(sorted(ch_t[g * G:(g + 1) * G].tolist())[-2:]) for g in range(n_group)]
+    granked = sorted(range(n_group), key=lambda g: (-gs[g], g))
+    admitted = [e for g in granked[:topk_group] for e in range(g * G, (g + 1) * G)]
+    best, best_sum = None, -math.inf
+    for comb in itertools.combinations(admitted, K):
+        v = sum(ch_t[list(comb)])
+        if v > best_sum:
+            best, best_sum = comb, v
+    vals = sorted(ch_t[admitted].tolist(), reverse=True)
+    egap = vals[K - 1] - vals[K] if K < len(vals) else math.inf
+    ggap = gs[granked[topk_group - 1]] - gs[granked[topk_group]] if topk_group < n_group else math.inf
+    return sorted(best), min(egap, ggap)
+
+
+def pin_group_bruteforce(O):
+    for name, over, ng, tg in (("tiny", {}, 4, 2),
+                               ("g2", dict(E=24, K=5, T=40, H=64, bias_halfwidth=0.2), 6, 3),
+                               ("g3", dict(E=12, K=2, T=30, H=64, bias_halfwidth=0.2), 12, 3)):
+        c = case(name, **over)
+        cfg = c["cfg"]
+        _, s, ch = choice_scores(c)
+        r = O.route(O.bf16_bits_to_f64(c["x"]), c["wr"], c["b"], cfg.K, cfg.routed_scaling,
+                    n_group=ng, topk_group=tg)
+        for t in range(cfg.T):
+            want, gap = _group_brute(ch[t], cfg.E, cfg.K, ng, tg)
+            assert gap > 1e-9, "case chosen to have no exact ties"
+            assert list(r.idx[t]) == want, f"token {t}: group-limited set differs from brute force"
+            assert abs(r.gap[t] - gap) <= 1e-12, f"token {t}: gap differs"
+        ssel = np.take_along_axis(s, r.idx.astype(np.int64), 1)
+        want_g = cfg.routed_scaling * ssel / ssel.sum(1, keepdims=True)
+        assert relerr(r.gate, want_g) < 1e-6, "gates: unbiased scores of the chosen set, renormalised"
+
+
+def pin_group_all_admitted_is_plain(O):
+    """With every group admitted the rule is the plain top-K over all experts."""
+    c = case("tiny")
+    cfg = c["cfg"]
+    _, _, ch = choice_scores(c)
+    combos = np.array(list(itertools.combinations(range(cfg.E), cfg.K)))
+    best = np.sort(combos[np.argmax(ch[:, combos].sum(-1), axis=1)], 1)
+    for ng in (1, 2, 4, 8):
+        r = O.route(O.bf16_bits_to_f64(c["x"]), c["wr"], c["b"], cfg.K, cfg.routed_scaling,
+                    n_group=ng, topk_group=ng)
+        assert np.array_equal(r.idx, best), f"n_group={ng}, all admitted: must equal the plain top-K"
+
+
+def pin_group_confinement(O):
+    c = case("g4", E=32, K=6, T=60, H=64, bias_halfwidth=0.3)
+    cfg = c["cfg"]
+    for ng, tg in ((8, 2), (4, 2), (16, 3)):
+        G = cfg.E // ng
+        r = O.route(O.bf16_bits_to_f64(c["x"]), c["wr"], c["b"], cfg.K, cfg.routed_scaling,
+                    n_group=ng, topk_group=tg)
+        groups = r.idx // G
+        assert all(len(set(row.tolist())) <= tg for row in groups), "experts from more groups than admitted"
+        assert np.all(np.diff(r.idx, axis=1) > 0) and np.all(r.gap >= 0)
+
+
+def pin_group_tie(O):
+    """Two groups with exactly equal scores: the lower group is admitted, gap 0."""
+    c = case("g5", E=8, K=2, T=16, H=64, bias_halfwidth=0.0)
+    wr = c["wr"].copy()
+    wr[6], wr[7] = wr[2], wr[3]           # group 3 mirrors group 1
+    b = np.zeros(8, np.float32)
+    b[[2, 3, 6, 7]] = 1.0
+    r = O.route(O.bf16_bits_to_f64(c["x"]), wr, b, 2, 5.0, n_group=4, topk_group=1)
+    assert np.array_equal(r.idx, np.tile([2, 3], (16, 1))), "equal group scores: lower group wins"
+    assert np.all(r.gap == 0.0)
+
+
+# ----------------------------------------------------------------------------
 # permutation
 # ----------------------------------------------------------------------------
 
@@ -353,6 +431,7 @@ def pin_mirror_grid(O):
 
 
 ALL_PINS = [
+    pin_group_bruteforce, pin_group_all_admitted_is_plain, pin_group_confinement, pin_group_tie,
     pin_bf16_conversions, pin_route_bruteforce, pin_route_bias_zero, pin_route_forced_and_gates,
     pin_route_invariants, pin_route_ties, pin_permute_bruteforce, pin_dense_masked,
     pin_dense_e1k1, pin_identity_expert, pin_zero_routed_path, pin_scale_linearity,

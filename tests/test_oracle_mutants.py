@@ -22,9 +22,15 @@ MUTANTS = {
                    "gate = (s_sel / s_sel.sum(axis=1, keepdims=True)).astype(np.float32)\n    return RouteResult"),
     "bias_ignored": ("choice = score + b[None, :]", "choice = score + 0.0 * b[None, :]"),
     "bias_subtracted": ("choice = score + b[None, :]", "choice = score - b[None, :]"),
-    "tie_to_higher_index": ("np.lexsort((experts, -choice[t]))", "np.lexsort((-experts, -choice[t]))"),
-    "top_k_plus_one": ("chosen = order[:K]", "chosen = order[1:K + 1] if K < E else order[:K]"),
-    "gap_wrong_neighbour": ("choice[t, order[K]] if K < E", "choice[t, order[min(K + 1, E - 1)]] if K < E"),
+    "tie_to_higher_index": ("np.lexsort((admitted, -c[admitted]))", "np.lexsort((-admitted, -c[admitted]))"),
+    "top_k_plus_one": ("chosen = order[:K]", "chosen = order[1:K + 1] if K < len(order) else order[:K]"),
+    "gap_wrong_neighbour": ("c[order[K]] if K < len(order)", "c[order[min(K + 1, len(order) - 1)]] if K < len(order)"),
+    "group_top1": ("[::-1][:2].sum()", "[::-1][:1].sum()"),
+    "group_sum_all": ("np.sort(c[g * G:(g + 1) * G])[::-1][:2].sum()", "c[g * G:(g + 1) * G].sum()"),
+    "group_score_unbiased": ("np.sort(c[g * G:(g + 1) * G])", "np.sort(score[t][g * G:(g + 1) * G])"),
+    "group_tie_to_higher": ("np.lexsort((groups, -gs))", "np.lexsort((-groups, -gs))"),
+    "group_one_too_many": ("gorder[:topk_group]]", "gorder[:topk_group + 1]]"),
+    "group_gap_ignored": ("gap[t] = min(egap, ggap)", "gap[t] = egap"),
     "relu_not_squared": ("return r * r", "return r"),
     "no_activation": ("r = np.maximum(a, 0.0)\n    return r * r", "return a"),
     "shared_dropped": ("+ hs @ bf16_bits_to_f64(w_sh_down_bits).T)", ")"),
