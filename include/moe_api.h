@@ -45,10 +45,22 @@ extern "C" {
 /* Sizes of one forward. T tokens, H hidden, L latent (moe_latent_size), E routed
  * experts, I expert intermediate, K experts per token, Is shared-expert
  * intermediate; routed_scaling multiplies the renormalised gates (5.0 in the
- * stated model, QA Q5.8). Host struct. */
+ * stated model, QA Q5.8). Host struct.
+ *
+ * n_group / topk_group: group-limited selection. The walkthrough section
+ * "路由与共享专家" takes the top-K within groups and QA Q9.2 has the layer
+ * inherit DeepseekV3MoE's routing; no page gives the group count, so the
+ * default (0 or 1 for both) is the plain top-K over all E experts. With
+ * n_group > 1 the E experts form n_group equal contiguous groups, a group's
+ * score is the sum of its two highest choice scores (its one score for
+ * one-expert groups), the topk_group best groups (equal scores: the lower
+ * group) admit their experts, and the top-K is taken among those. Requires
+ * E % n_group == 0, 1 <= topk_group <= n_group, K <= topk_group * E / n_group
+ * (else MOE_ERR_INVALID) and n_group <= 64 (else MOE_ERR_UNSUPPORTED). */
 typedef struct moe_dims {
   int32_t T, H, L, E, I, K, Is;
   float routed_scaling;
+  int32_t n_group, topk_group;
 } moe_dims;
 
 /* Weights, all device pointers, all [out, in] row-major.
@@ -73,7 +85,7 @@ typedef struct moe_weights {
 
 enum moe_status {
   MOE_OK = 0,
-  MOE_ERR_INVALID = -1,      /* null pointer, non-positive size, K > E, bad C */
+  MOE_ERR_INVALID = -1,      /* null pointer, non-positive size, K > E, bad C, bad groups */
   MOE_ERR_UNSUPPORTED = -2,  /* H, L, I or Is not a multiple of 64; E > 1024; K > 64;
                                 T*K >= 2^31; 2*T*L >= 2^32 */
   MOE_ERR_WORKSPACE = -3,    /* workspace null, too small or not 256-byte aligned */
@@ -91,15 +103,17 @@ typedef struct moe_ws_layout {
 } moe_ws_layout;
 
 /* Router: fp32 logits, sigmoid, bias-adjusted top-K, renormalised and scaled gates.
- * (QA Q5.2, Q5.3, Q5.8; walkthrough "路由与共享专家"). Reads T, H, E, K and
- * routed_scaling of dims (the other fields are ignored).
+ * (QA Q5.2, Q5.3, Q5.8; walkthrough "路由与共享专家"). Reads T, H, E, K,
+ * routed_scaling, n_group and topk_group of dims (the other fields are ignored).
  *   x         device [T,H] bf16
  *   w_router  device [E,H] fp32;  corr_bias device [E] fp32
  *   topk_idx  device [T,K] int32 out: chosen experts, ascending per token
  *   topk_gate device [T,K] fp32 out: routed_scaling * s / sum(s) over the chosen
  *   topk_gap  device [T]   fp32 out, may be NULL: c_(K) - c_(K+1), the margin
- *             between the last chosen and the first unchosen choice score in
- *             descending order (+inf when K == E)
+ *             between the last chosen and the first unchosen admitted choice
+ *             score in descending order (+inf when every admitted expert is
+ *             chosen); with groups, the smaller of that and the margin between
+ *             the last admitted and the first refused group score
  *   ws        device workspace of at least moe_route_workspace_bytes(dims) bytes,
  *             256-byte aligned
  * The logits are accumulated in fp32 from exact bf16 x fp32 products (the fp32

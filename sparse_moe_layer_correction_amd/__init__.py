@@ -49,7 +49,7 @@ class MoEError(RuntimeError):
 class _Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("I", ctypes.c_int32), ("K", ctypes.c_int32), ("Is", ctypes.c_int32),
-                ("routed_scaling", ctypes.c_float)]
+                ("routed_scaling", ctypes.c_float), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -74,9 +74,12 @@ class MoEDims:
     K: int
     Is: int
     routed_scaling: float = 5.0
+    n_group: int = 1          # group-limited routing (1 / 1: plain top-K over all experts)
+    topk_group: int = 1
 
     def c(self) -> _Dims:
-        return _Dims(self.T, self.H, self.L, self.E, self.I, self.K, self.Is, self.routed_scaling)
+        return _Dims(self.T, self.H, self.L, self.E, self.I, self.K, self.Is, self.routed_scaling,
+                     self.n_group, self.topk_group)
 
 
 _lib = None
@@ -193,7 +196,7 @@ def workspace_layout(dims: MoEDims) -> Dict[str, int]:
 # ----------------------------------------------------------------------------
 
 def route(x, w_router, corr_bias, K: int, routed_scaling: float = 5.0, *, with_gap: bool = True,
-          ws=None, stream=None):
+          ws=None, stream=None, n_group: int = 1, topk_group: int = 1):
     """Router: returns (topk_idx [T,K] int32, topk_gate [T,K] fp32, gap [T] fp32 or None)."""
     torch = _torch()
     T, H = x.shape
@@ -202,7 +205,7 @@ def route(x, w_router, corr_bias, K: int, routed_scaling: float = 5.0, *, with_g
     _need(x, "x", torch.bfloat16, (T, H), dev)
     _need(w_router, "w_router", torch.float32, (E, H), dev)
     _need(corr_bias, "corr_bias", torch.float32, (E,), dev)
-    dims = MoEDims(T, H, 64, E, 64, K, 64, routed_scaling)
+    dims = MoEDims(T, H, 64, E, 64, K, 64, routed_scaling, n_group, topk_group)
     d = dims.c()
     lib = load_library()
     idx = torch.empty(T, K, dtype=torch.int32, device=dev)
@@ -261,18 +264,20 @@ def _weight_struct(dims: MoEDims, w: Dict, dev):
     return _Weights(*[_ptr(w[n]) for n in _WEIGHT_SPECS])
 
 
-def dims_from(x, weights: Dict, K: int, routed_scaling: float = 5.0) -> MoEDims:
+def dims_from(x, weights: Dict, K: int, routed_scaling: float = 5.0, n_group: int = 1,
+              topk_group: int = 1) -> MoEDims:
     T, H = x.shape
     E, I, L = weights["w_up"].shape
     Is = weights["w_sh_up"].shape[0]
-    return MoEDims(T, H, L, E, I, K, Is, routed_scaling)
+    return MoEDims(T, H, L, E, I, K, Is, routed_scaling, n_group, topk_group)
 
 
-def forward(x, weights: Dict, K: int, routed_scaling: float = 5.0, *, out=None, ws=None, stream=None):
+def forward(x, weights: Dict, K: int, routed_scaling: float = 5.0, *, out=None, ws=None, stream=None,
+            n_group: int = 1, topk_group: int = 1):
     """Whole layer forward; returns out [T,H] bf16. ``ws`` (uint8, >= workspace_bytes) keeps
     the intermediates at the offsets of ``workspace_layout``."""
     torch = _torch()
-    dims = dims_from(x, weights, K, routed_scaling)
+    dims = dims_from(x, weights, K, routed_scaling, n_group, topk_group)
     dev = x.device
     _need(x, "x", torch.bfloat16, (dims.T, dims.H), dev)
     wstruct = _weight_struct(dims, weights, dev)

@@ -10,6 +10,7 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
+constexpr int kMaxGroups = 64;      // one group per lane of the top-K wave
 
 // GEMM tile configurations (BM x BN; 256x256 runs 8 waves, the others 4).
 // TILE_256x256_GROUPED: the grouped expert products (one problem per launch).
@@ -55,7 +56,7 @@ struct PermuteScratch {
 
 hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* parts, hipStream_t st);
 hipError_t launch_topk(const float* logits, int64_t ldl, const float* bias, int T, int E, int K, float scale,
-                       int32_t* idx, float* gate, float* gap, hipStream_t st);
+                       int n_group, int topk_group, int32_t* idx, float* gate, float* gap, hipStream_t st);
 hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, const PermuteScratch& ps,
                                int32_t* offsets, int32_t* row_token, int32_t* slot_row, hipStream_t st);
 hipError_t launch_gather_rows(const uint16_t* src, int C, const int32_t* row_token, int64_t rows, uint16_t* dst,

@@ -53,13 +53,23 @@ struct Layout {
 // Which fields of moe_dims a call reads.
 enum DimsUse { USE_ROUTE = 1, USE_PERMUTE = 2, USE_ALL = 3 };
 
+// Group-limited routing: 0 in either field means the plain top-K (1 group).
+int groups_of(const moe_dims& d) { return d.n_group == 0 ? 1 : d.n_group; }
+int topk_groups_of(const moe_dims& d) { return d.topk_group == 0 ? 1 : d.topk_group; }
+
 bool dims_ok(const moe_dims* d, int* status, int use = USE_ALL) {
   *status = MOE_ERR_INVALID;
   if (d == nullptr) return false;
   if (d->T <= 0 || d->E <= 0 || d->K <= 0 || d->K > d->E) return false;
   if ((use & USE_ROUTE) && d->H <= 0) return false;
   if (use == USE_ALL && (d->L <= 0 || d->I <= 0 || d->Is <= 0)) return false;
+  if (use & USE_ROUTE) {
+    const int ng = groups_of(*d), tg = topk_groups_of(*d);
+    if (ng < 1 || tg < 1 || tg > ng || d->E % ng) return false;
+    if ((int64_t)d->K > (int64_t)tg * (d->E / ng)) return false;
+  }
   *status = MOE_ERR_UNSUPPORTED;
+  if ((use & USE_ROUTE) && groups_of(*d) > kMaxGroups) return false;
   if (d->E > kMaxExperts || d->K > kMaxTopK) return false;
   if ((use & USE_ROUTE) && d->H % 64) return false;
   if (use == USE_ALL && (d->L % 64 || d->I % 64 || d->Is % 64)) return false;
@@ -75,7 +85,7 @@ bool dims_ok(const moe_dims* d, int* status, int use = USE_ALL) {
 // moe_dims with the fields a partial call does not read zeroed, for the layout.
 moe_dims only_used(const moe_dims& d, int use) {
   moe_dims u = d;
-  if (!(use & USE_ROUTE)) u.H = 0;
+  if (!(use & USE_ROUTE)) { u.H = 0; u.n_group = 0; u.topk_group = 0; }
   if (use != USE_ALL) { u.L = 0; u.I = 0; u.Is = 0; }
   return u;
 }
@@ -236,7 +246,8 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (mk.mark(MOE_PHASE_TOPK) != hipSuccess) return MOE_ERR_HIP;
-  e = launch_topk(logits, l.ldl, bias, d.T, d.E, d.K, d.routed_scaling, idx, gate, gap, st);
+  e = launch_topk(logits, l.ldl, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d), topk_groups_of(d), idx, gate,
+                  gap, st);
   return hip_status(e);
 }
 
@@ -253,15 +264,16 @@ PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 100; }
+int moe_abi_version(void) { return 101; }
 
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";
-    case MOE_ERR_INVALID: return "invalid argument (null pointer, non-positive size, K > E or bad row length)";
+    case MOE_ERR_INVALID:
+      return "invalid argument (null pointer, non-positive size, K > E, bad row length or bad expert groups)";
     case MOE_ERR_UNSUPPORTED:
       return "unsupported size (H, L, I, Is must be multiples of 64; E <= 1024; K <= 64; T*K < 2^31; "
-             "2*T*L < 2^32)";
+             "2*T*L < 2^32; n_group <= 64)";
     case MOE_ERR_WORKSPACE: return "workspace null, too small or not 256-byte aligned";
     case MOE_ERR_HIP: return "HIP launch error";
     default: return "unknown status";

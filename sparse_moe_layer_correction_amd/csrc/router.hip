@@ -13,7 +13,8 @@
 // then the complement of the expert index, so equal choices go to the lower
 // index), a ballot-based rank that lists the chosen experts in ascending index,
 // and gates = routed_scaling * s / sum(s) over the chosen set (walkthrough
-// section "路由与共享专家"; QA Q5.8).
+// section "路由与共享专家"; QA Q5.8). Optionally the choice is first limited to
+// the best groups of experts (see topk_kernel).
 #include "kernels.h"
 
 namespace moe {
@@ -38,8 +39,9 @@ __global__ void split_router_weight_kernel(const float* __restrict__ w, int64_t 
 template <int VPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int64_t ldl,
                                                    const float* __restrict__ bias, int T, int E, int K,
-                                                   float scale, int32_t* __restrict__ idx,
-                                                   float* __restrict__ gate, float* __restrict__ gap) {
+                                                   float scale, int n_group, int topk_group,
+                                                   int32_t* __restrict__ idx, float* __restrict__ gate,
+                                                   float* __restrict__ gap) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -61,6 +63,58 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     }
   }
 
+  // Group-limited selection (walkthrough "路由与共享专家": top-K within
+  // groups; the DeepSeek-V3 rule of the parent class, QA Q9.2): group g is
+  // experts [g*G, (g+1)*G); its score is the sum of its two highest choice
+  // scores. Lane g keeps group g's score; topk_group rounds of a wave arg-max
+  // over (score, lower group first) admit groups, and the experts of the other
+  // groups drop out of the choice (key 0 never wins).
+  float ggap = __builtin_inff();
+  int admitted = E;
+  if (n_group > 1) {
+    const int G = E / n_group;
+    uint64_t gkey = 0;
+    for (int g = 0; g < n_group; ++g) {
+      uint64_t b1 = 0;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int e = j * 64 + lane;
+        if (e < E && e / G == g && key[j] > b1) b1 = key[j];
+      }
+      b1 = wave_max_u64(b1);
+      float gs = f32_from_order_key((uint32_t)(b1 >> 32));
+      if (G > 1) {
+        uint64_t b2 = 0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int e = j * 64 + lane;
+          if (e < E && e / G == g && key[j] != b1 && key[j] > b2) b2 = key[j];
+        }
+        b2 = wave_max_u64(b2);
+        gs += f32_from_order_key((uint32_t)(b2 >> 32));
+      }
+      if (lane == g) gkey = ((uint64_t)f32_order_key(gs) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)g);
+    }
+    uint64_t allowed = 0, glast = 0;
+    for (int r = 0; r < topk_group; ++r) {
+      const uint64_t best = wave_max_u64(gkey);
+      glast = best;
+      const int g = (int)(0xFFFFFFFFu - (uint32_t)best);
+      allowed |= 1ull << g;
+      if (lane == g) gkey = 0;
+    }
+    if (topk_group < n_group) {
+      const uint64_t next = wave_max_u64(gkey);
+      ggap = f32_from_order_key((uint32_t)(glast >> 32)) - f32_from_order_key((uint32_t)(next >> 32));
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int e = j * 64 + lane;
+      if (e < E && !((allowed >> (e / G)) & 1ull)) key[j] = 0;
+    }
+    admitted = topk_group * G;
+  }
+
   uint32_t taken = 0;
   uint64_t kth = 0;
   for (int k = 0; k < K; ++k) {
@@ -75,7 +129,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   }
 
   float gapv = __builtin_inff();
-  if (K < E) {
+  if (K < admitted) {
     uint64_t best = 0;
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
@@ -83,6 +137,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     best = wave_max_u64(best);
     gapv = f32_from_order_key((uint32_t)(kth >> 32)) - f32_from_order_key((uint32_t)(best >> 32));
   }
+  gapv = fminf(gapv, ggap);
 
   float ssum = 0.f;
 #pragma unroll
@@ -114,14 +169,19 @@ hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* pa
 }
 
 hipError_t launch_topk(const float* logits, int64_t ldl, const float* bias, int T, int E, int K,
-                       float scale, int32_t* idx, float* gate, float* gap, hipStream_t st) {
+                       float scale, int n_group, int topk_group, int32_t* idx, float* gate, float* gap,
+                       hipStream_t st) {
   const dim3 grid((T + 3) / 4), block(256);
   const int vpl = (E + 63) / 64;
-  if (vpl <= 1) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, st, logits, ldl, bias, T, E, K, scale, idx, gate, gap);
-  else if (vpl <= 2) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, st, logits, ldl, bias, T, E, K, scale, idx, gate, gap);
-  else if (vpl <= 4) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, st, logits, ldl, bias, T, E, K, scale, idx, gate, gap);
-  else if (vpl <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, st, logits, ldl, bias, T, E, K, scale, idx, gate, gap);
-  else hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, logits, ldl, bias, T, E, K, scale, idx, gate, gap);
+#define MOE_TOPK(V)                                                                                           \
+  hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, st, logits, ldl, bias, T, E, K, scale, n_group, topk_group, \
+                     idx, gate, gap)
+  if (vpl <= 1) MOE_TOPK(1);
+  else if (vpl <= 2) MOE_TOPK(2);
+  else if (vpl <= 4) MOE_TOPK(4);
+  else if (vpl <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

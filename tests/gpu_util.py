@@ -66,14 +66,14 @@ def weights_of(d):
     return {k: d[k] for k in ("w_router", "corr_bias", "w_fc1", "w_up", "w_down", "w_fc2", "w_sh_up", "w_sh_down")}
 
 
-def oracle_route(d, tokens=None):
+def oracle_route(d, tokens=None, n_group=1, topk_group=1):
     cfg = d["cfg"]
     x = d["x"] if tokens is None else d["x"][tokens]
     return oracle.route(oracle.bf16_bits_to_f64(u16(x)), host_f32(d["w_router"]), host_f32(d["corr_bias"]),
-                        cfg.K, cfg.routed_scaling)
+                        cfg.K, cfg.routed_scaling, n_group=n_group, topk_group=topk_group)
 
 
-def oracle_forward_tokens(d, tokens, idx_override=None, mirror=True, keep=False):
+def oracle_forward_tokens(d, tokens, idx_override=None, mirror=True, keep=False, n_group=1, topk_group=1):
     """The oracle on a subset of tokens (tokens are independent), experts copied on demand."""
     cfg = d["cfg"]
     cache = {}
@@ -85,7 +85,8 @@ def oracle_forward_tokens(d, tokens, idx_override=None, mirror=True, keep=False)
 
     return oracle.forward(u16(d["x"][tokens]), host_f32(d["w_router"]), host_f32(d["corr_bias"]),
                           u16(d["w_fc1"]), u16(d["w_fc2"]), u16(d["w_sh_up"]), u16(d["w_sh_down"]),
-                          expert, cfg.K, cfg.routed_scaling, mirror=mirror, idx_override=idx_override, keep=keep)
+                          expert, cfg.K, cfg.routed_scaling, mirror=mirror, idx_override=idx_override, keep=keep,
+                          n_group=n_group, topk_group=topk_group)
 
 
 def check_routing(idx_gpu, gate_gpu, gap_gpu, ref, label=""):
@@ -114,6 +115,39 @@ def check_routing(idx_gpu, gate_gpu, gap_gpu, ref, label=""):
         assert np.all(np.isinf(gg[~fin]))
         err = np.max(np.abs(gg[fin] - ref.gap[fin])) if fin.any() else 0.0
         assert err < 1e-5, f"{label}: gap error {err:.3g}"
+    return int(flagged.sum())
+
+
+def check_group_routing(idx_gpu, gate_gpu, gap_gpu, ref, n_group, topk_group, label=""):
+    """check_routing for group-limited selection. Flagged tokens (group or expert
+    margin inside the tie band) must use at most topk_group groups and be a top-K,
+    within the band, of the experts of the groups they use."""
+    idx_gpu = np.asarray(idx_gpu)
+    T, K = idx_gpu.shape
+    E = ref.choice.shape[1]
+    G = E // n_group
+    flagged = ref.gap < oracle.GAP_FLAG
+    ok = ~flagged
+    mism = np.nonzero(np.any(idx_gpu[ok] != ref.idx[ok], axis=1))[0]
+    assert mism.size == 0, f"{label}: {mism.size} unflagged tokens route differently (first {np.nonzero(ok)[0][mism[:5]]})"
+    for t in np.nonzero(flagged)[0]:
+        groups = np.unique(idx_gpu[t] // G)
+        assert len(groups) <= topk_group and len(np.unique(idx_gpu[t])) == K, f"{label}: token {t}"
+        pool = np.concatenate([np.arange(g * G, (g + 1) * G) for g in groups])
+        c = ref.choice[t]
+        kth = np.sort(c[pool])[::-1][K - 1]
+        assert np.all(c[idx_gpu[t]] >= kth - oracle.GAP_FLAG), f"{label}: token {t} outside the tie band"
+    same = np.all(idx_gpu == ref.idx, axis=1)
+    g = np.asarray(gate_gpu)[same].astype(np.float64)
+    gr = ref.gate[same].astype(np.float64)
+    if g.size:
+        rel = np.max(np.abs(g - gr) / np.abs(gr))
+        assert rel <= GATE_RTOL, f"{label}: gate relative error {rel:.3g}"
+    gg = np.asarray(gap_gpu, dtype=np.float64)
+    fin = np.isfinite(ref.gap)
+    assert np.all(np.isinf(gg[~fin]))
+    err = np.max(np.abs(gg[fin] - ref.gap[fin])) if fin.any() else 0.0
+    assert err < 1e-5, f"{label}: gap error {err:.3g}"
     return int(flagged.sum())
 
 

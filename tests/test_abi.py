@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 100
+    assert lib.moe_abi_version() == 101
 
 
 def test_status_strings(lib):
@@ -98,6 +98,9 @@ def test_workspace_sizes_at_every_token_count(lib, T):
     (dict(E=2048, K=4), -2), (dict(K=65, E=100), -2),
     # gathered latent rows are addressed with 32-bit byte offsets: 2*T*L < 2^32
     (dict(T=1 << 20, L=2048), -2), (dict(T=1 << 28, K=8), -2),
+    # expert groups: E divisible, topk_group within n_group, K within the admitted experts, <= 64 groups
+    (dict(n_group=3), -1), (dict(n_group=4, topk_group=5), -1), (dict(n_group=4, topk_group=1, K=5), -1),
+    (dict(n_group=-2), -1), (dict(E=256, n_group=128, topk_group=2), -2),
 ])
 def test_forward_rejects_bad_dims(lib, bad, code):
     base = dict(T=TINY.T, H=TINY.H, L=TINY.L, E=TINY.E, I=TINY.I, K=TINY.K, Is=TINY.Is)
@@ -136,3 +139,11 @@ def test_python_binding_refuses_cpu_tensors():
     b = torch.zeros(8)
     with pytest.raises(ValueError):
         M.route(x, wr, b, 2)
+
+
+@pytest.mark.parametrize("ng,tg", [(0, 0), (1, 1), (4, 2), (16, 4), (4, 4)])
+def test_expert_groups_accepted(lib, ng, tg):
+    d = M.MoEDims(T=TINY.T, H=TINY.H, L=TINY.L, E=TINY.E, I=TINY.I, K=TINY.K, Is=TINY.Is,
+                  n_group=ng, topk_group=tg)
+    assert lib.moe_workspace_bytes(_d(d)) > 0
+    assert lib.moe_route_workspace_bytes(_d(d)) > 0

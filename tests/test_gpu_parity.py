@@ -12,8 +12,8 @@ import torch
 import oracle
 import sparse_moe_layer_correction_amd as M
 import workloads as W
-from gpu_util import (OUT_TOL, bf16_dev_to_f64, check_routing, device_inputs, host_f32, log,
-                      oracle_forward_tokens, oracle_route, relerr, u16, weights_of)
+from gpu_util import (OUT_TOL, bf16_dev_to_f64, check_group_routing, check_routing, device_inputs, host_f32,
+                      log, oracle_forward_tokens, oracle_route, relerr, u16, weights_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,6 +98,52 @@ def test_route_ties_go_to_lower_index():
     idx, _, gap = run_route(d)
     assert np.array_equal(idx, np.tile([0, 1, 2, 3], (d["cfg"].T, 1)))
     assert np.all(gap == 0.0)
+
+
+# ----------------------------------------------------------------------------
+# group-limited router
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,over,ng,tg", [
+    ("tiny", {}, 4, 2),
+    ("tiny", {}, 8, 4),
+    ("tiny", {}, 16, 4),                     # one-expert groups
+    ("tiny", dict(T=37), 4, 1),              # one group admitted: K = its size
+    ("nano", dict(T=1024), 8, 4),
+    ("ultra_prefill", {}, 8, 4),             # the Ultra router at full size
+])
+def test_route_groups_parity(name, over, ng, tg):
+    d = device_inputs(name, **over)
+    cfg = d["cfg"]
+    log(f"[route-groups] {cfg.name} T={cfg.T} E={cfg.E} K={cfg.K} n_group={ng} topk_group={tg}")
+    idx, gate, gap = M.route(d["x"], d["w_router"], d["corr_bias"], cfg.K, cfg.routed_scaling,
+                             n_group=ng, topk_group=tg)
+    torch.cuda.synchronize()
+    ref = oracle_route(d, n_group=ng, topk_group=tg)
+    n_flag = check_group_routing(idx.cpu().numpy(), gate.cpu().numpy(), gap.cpu().numpy(), ref, ng, tg,
+                                 f"{name}{over} groups {ng}/{tg}")
+    log(f"[route-groups] {name}: {n_flag} of {cfg.T} tokens in the tie band")
+
+
+def test_forward_groups_tiny_full():
+    d = device_inputs("tiny")
+    cfg = d["cfg"]
+    ng, tg = 4, 2
+    dims = M.dims_from(d["x"], weights_of(d), cfg.K, cfg.routed_scaling, ng, tg)
+    ws = torch.empty(M.workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out = M.forward(d["x"], weights_of(d), cfg.K, cfg.routed_scaling, ws=ws, n_group=ng, topk_group=tg)
+    torch.cuda.synchronize()
+    lay = M.workspace_layout(dims)
+    idx = ws_view(ws, lay, "idx", torch.int32, (cfg.T, cfg.K)).cpu().numpy()
+    tokens = np.arange(cfg.T)
+    ref_r = oracle_route(d, tokens, n_group=ng, topk_group=tg)
+    assert np.array_equal(idx, ref_r.idx), "tiny has no tie band: routing must be identical"
+    ref = oracle_forward_tokens(d, tokens, n_group=ng, topk_group=tg)
+    e = relerr(bf16_dev_to_f64(out), ref["out"])
+    log(f"[parity] tiny groups {ng}/{tg}: out {e:.2e}")
+    assert e < OUT_TOL
+    # the grouped routing must differ from the plain one somewhere, else the test shows nothing
+    assert not np.array_equal(ref_r.idx, oracle_route(d, tokens).idx)
 
 
 # ----------------------------------------------------------------------------
