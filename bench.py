@@ -73,6 +73,28 @@ def cpu_baseline(d, cfg, idx_gpu, n_tokens: int):
                       f"{os.cpu_count()} host cores, BLAS threads {threads}"}
 
 
+def graph_ms_per_step(M, d, weights, cfg, out, ws, steps: int) -> float:
+    """Capture one forward into a HIP graph (torch.cuda.CUDAGraph) and time its replays."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            M.forward(d["x"], weights, cfg.K, cfg.routed_scaling, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.forward(d["x"], weights, cfg.K, cfg.routed_scaling, out=out, ws=ws)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return 1e3 * (time.perf_counter() - t0) / steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +211,12 @@ def main():
         "events_ms_per_step": round(ev_ms, 4),
         "roofline": roofline,
     }
+    if cfg.T <= 64:
+        # the same forward captured once into a HIP graph and replayed: what a
+        # serving loop that replays captured decode steps pays per step
+        g_ms = graph_ms_per_step(M, d, weights, cfg, out, ws, args.steps)
+        result["graph_ms_per_step"] = round(g_ms, 4)
+        result["graph_tokens_per_s"] = round(cfg.T / (g_ms / 1e3), 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, cfg, idx_gpu, args.cpu_tokens)
     if args.calibrate_copy:
