@@ -2,10 +2,10 @@
 //
 // Each expert's output row is multiplied by its token's gate and the K rows are
 // summed in the latent space, before fc2 ("Nemotron 3 Ultra 架构 QA", Q5.5
-// point 3 and Q5.1). Written as a gather: one wavefront per token reads its K
-// permuted rows (16 bytes per lane, consecutive lanes on consecutive columns)
-// and sums them in fp32 in slot order, so the result is deterministic without
-// atomics. The sum is rounded once to bf16.
+// point 3 and Q5.1). Written as a gather: one wavefront per token and 512
+// columns reads its K permuted rows (16 bytes per lane, consecutive lanes on
+// consecutive columns) and sums them in fp32 in slot order, so the result is
+// deterministic without atomics. The sum is rounded once to bf16.
 #include "kernels.h"
 
 namespace moe {
@@ -13,64 +13,64 @@ namespace moe {
 __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ gate,
                                                       const int32_t* __restrict__ slot_row, int T, int K, int L,
                                                       uint16_t* __restrict__ y_lat) {
+  // one wavefront per (token, 512-column chunk): few tokens still spread over
+  // several waves, and each wave keeps up to 8 rows in flight
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int nchunk = (L + 511) / 512;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (int64_t)T * nchunk) return;
+  const int t = (int)(w / nchunk);
+  const int cb = (int)(w % nchunk) * 512;
   // lane k < K holds slot k's row and gate (K <= 64)
   const int my_row = lane < K ? slot_row[(int64_t)t * K + lane] : 0;
   const float my_g = lane < K ? gate[(int64_t)t * K + lane] : 0.f;
 
   // every lane runs every iteration (the shuffles need all lanes); only the
   // loads and the store are guarded when L is not a multiple of 512
-  for (int cb = 0; cb < L; cb += 512) {
-    const int c0 = cb + lane * 8;
-    const bool act = c0 < L;
-    const int64_t col = act ? c0 : 0;
-    float acc[8];
+  const int c0 = cb + lane * 8;
+  const bool act = c0 < L;
+  const int64_t col = act ? c0 : 0;
+  float acc[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-    int k = 0;
-    for (; k + 4 <= K; k += 4) {
-      u32x4 v[4];
-      float g[4];
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  auto add = [&](const u32x4& v, float g) {
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = __shfl(my_row, k + u, 64);
-        g[u] = __shfl(my_g, k + u, 64);
-        v[u] = *reinterpret_cast<const u32x4*>(y + (int64_t)r * L + col);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += g[u] * bf16_bits_to_f32(w[q] & 0xFFFFu);
-          acc[2 * q + 1] += g[u] * bf16_bits_to_f32(w[q] >> 16);
-        }
-      }
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += g * bf16_bits_to_f32(wv[q] & 0xFFFFu);
+      acc[2 * q + 1] += g * bf16_bits_to_f32(wv[q] >> 16);
     }
-    for (; k < K; ++k) {
-      const int r = __shfl(my_row, k, 64);
-      const float g = __shfl(my_g, k, 64);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(y + (int64_t)r * L + col);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  };
+  int k = 0;
+  for (; k + 8 <= K; k += 8) {
+    u32x4 v[8];
+    float g[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += g * bf16_bits_to_f32(w[q] & 0xFFFFu);
-        acc[2 * q + 1] += g * bf16_bits_to_f32(w[q] >> 16);
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int r = __shfl(my_row, k + u, 64);
+      g[u] = __shfl(my_g, k + u, 64);
+      v[u] = *reinterpret_cast<const u32x4*>(y + (int64_t)r * L + col);
     }
-    if (act) {
-      const u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                       pack_bf16x2(acc[6], acc[7])};
-      *reinterpret_cast<u32x4*>(y_lat + (int64_t)t * L + c0) = o;
-    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(v[u], g[u]);     // slot order
+  }
+  for (; k < K; ++k) {
+    const int r = __shfl(my_row, k, 64);
+    const float g = __shfl(my_g, k, 64);
+    add(*reinterpret_cast<const u32x4*>(y + (int64_t)r * L + col), g);
+  }
+  if (act) {
+    const u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                     pack_bf16x2(acc[6], acc[7])};
+    *reinterpret_cast<u32x4*>(y_lat + (int64_t)t * L + c0) = o;
   }
 }
 
 hipError_t launch_combine(const uint16_t* y, const float* gate, const int32_t* slot_row, int T, int K, int L,
                           uint16_t* y_lat, hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel, dim3((T + 3) / 4), dim3(256), 0, st, y, gate, slot_row, T, K, L, y_lat);
+  const int64_t waves = (int64_t)T * ((L + 511) / 512);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, y, gate, slot_row, T, K, L,
+                     y_lat);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@
 //  4. scatter: slot (t,k) of expert e goes to row
 //       offsets[e] + base[e][t/64] + popcount(mask[e][t/64] below bit t%64).
 //  5. gather: dst[r] = src[row_token[r]] with 16-byte loads and stores.
+// With at most 64 tokens, steps 1-4 run as one workgroup (permute_small_kernel).
 #include "kernels.h"
 
 namespace moe {
@@ -49,20 +50,16 @@ __global__ void __launch_bounds__(256) expert_scan_kernel(const uint64_t* __rest
   if (lane == 0) counts[e] = running;
 }
 
-// One workgroup of 1024 threads (E <= 1024).
-// One workgroup of 1024 threads (E <= 1024). Also lists the experts that
-// received at least one token, in ascending order.
-__global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict__ counts, int E, int BM,
-                                                       int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ tile_e,
-                                                       int32_t* __restrict__ tile_m0,
-                                                       int32_t* __restrict__ n_mtiles,
-                                                       int32_t* __restrict__ touched,
-                                                       int32_t* __restrict__ n_touched,
-                                                       int32_t* __restrict__ first_mtile) {
+// Expert offsets and the grouped products' M-tile table from the per-expert
+// count c of thread tid (one workgroup of 1024 threads, E <= 1024). Also lists
+// the experts that received at least one token, in ascending order. Returns
+// the exclusive offset of expert tid.
+__device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_m0,
+                                              int32_t* __restrict__ n_mtiles, int32_t* __restrict__ touched,
+                                              int32_t* __restrict__ n_touched, int32_t* __restrict__ first_mtile) {
   __shared__ int wsum_c[16], wsum_t[16], wsum_h[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid < E ? counts[tid] : 0;
   const int nt = (c + BM - 1) / BM;
   const int hit = c > 0 ? 1 : 0;
   const int ic = wave_inclusive_scan_i32(c);
@@ -86,6 +83,58 @@ __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict
     offsets[E] = ex_c + c;
     *n_mtiles = ex_t + nt;
     *n_touched = ex_h + hit;
+  }
+  return ex_c;
+}
+
+__global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict__ counts, int E, int BM,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ tile_e,
+                                                       int32_t* __restrict__ tile_m0,
+                                                       int32_t* __restrict__ n_mtiles,
+                                                       int32_t* __restrict__ touched,
+                                                       int32_t* __restrict__ n_touched,
+                                                       int32_t* __restrict__ first_mtile) {
+  const int c = (int)threadIdx.x < E ? counts[threadIdx.x] : 0;
+  layout_experts(c, E, BM, offsets, tile_e, tile_m0, n_mtiles, touched, n_touched, first_mtile);
+}
+
+// All of steps 1-4 in one workgroup when the tokens fit one 64-token block
+// (T <= 64): the masks and offsets stay in LDS, and a few-token forward pays
+// one launch instead of four.
+__global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx, int T, int K, int E,
+                                                             int BM, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tile_e,
+                                                             int32_t* __restrict__ tile_m0,
+                                                             int32_t* __restrict__ n_mtiles,
+                                                             int32_t* __restrict__ touched,
+                                                             int32_t* __restrict__ n_touched,
+                                                             int32_t* __restrict__ first_mtile,
+                                                             int32_t* __restrict__ row_token,
+                                                             int32_t* __restrict__ slot_row) {
+  __shared__ unsigned long long m[kMaxExperts];
+  __shared__ int off[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int tk = T * K;
+  for (int e = tid; e < E; e += blockDim.x) m[e] = 0ull;
+  __syncthreads();
+  for (int s = tid; s < tk; s += blockDim.x) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicOr(&m[e], 1ull << (s / K));
+  }
+  __syncthreads();
+  const int c = tid < E ? __popcll(m[tid]) : 0;
+  const int ex = layout_experts(c, E, BM, offsets, tile_e, tile_m0, n_mtiles, touched, n_touched, first_mtile);
+  if (tid < E) off[tid] = ex;
+  __syncthreads();
+  for (int s = tid; s < tk; s += blockDim.x) {
+    const int t = s / K;
+    const int e = idx[s];
+    if (e < 0 || e >= E) { slot_row[s] = -1; continue; }
+    const uint64_t below = t == 0 ? 0ull : (m[e] & (~0ull >> (64 - t)));
+    const int r = off[e] + __popcll(below);
+    row_token[r] = t;
+    slot_row[s] = r;
   }
 }
 
@@ -126,6 +175,11 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(const uint16_t* __rest
 hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, const PermuteScratch& ps,
                                int32_t* offsets, int32_t* row_token, int32_t* slot_row, hipStream_t st) {
   const int nblk = (T + 63) / 64;
+  if (nblk == 1) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, T, K, E, BM, offsets, ps.tile_e,
+                       ps.tile_m0, ps.n_mtiles, ps.touched, ps.n_touched, ps.first_mtile, row_token, slot_row);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(block_masks_kernel, dim3(nblk), dim3(256), 0, st, idx, T, K, E, nblk, ps.masks);
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, st, ps.masks, nblk, E, ps.base, ps.counts);
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, ps.counts, E, BM, offsets, ps.tile_e, ps.tile_m0,
