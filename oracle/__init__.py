@@ -3,3 +3,5 @@ imported by the tests, the smoke check and the benchmark's CPU-baseline leg, and
 by nothing on the library path."""
 from .moe_oracle import *  # noqa: F401,F403
 from .moe_oracle import __all__  # noqa: F401
+from .mxfp8 import (MX_BLOCK, dequantize_mxfp8, e4m3_decode, e4m3_encode,  # noqa: F401
+                    quantize_mxfp8)
