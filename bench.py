@@ -1,6 +1,6 @@
 """Benchmark of the LatentMoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ultra_prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ultra_prefill] [--experts bf16|mxfp8]
 
 A step is one whole forward (router, permutation, fc1 + shared up, expert up,
 expert down, combine, fc2 + shared down) over one batch of seeded synthetic
@@ -26,22 +26,29 @@ METRIC = "LatentMoE fwd tokens/s + TFLOP/s (Ultra shape); % MFMA peak / % HBM BW
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def phase_work(cfg, n_touched: int):
+# bytes per routed-expert weight element: bf16, or an E4M3 code plus 1/32 of an E8M0 scale
+EXPERT_WEIGHT_BYTES = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32}
+
+
+def phase_work(cfg, n_touched: int, experts: str = "bf16"):
     """Algorithmic FLOPs and compulsory HBM bytes of each phase of one forward."""
     T, H, L, E, I, K, Is = cfg.T, cfg.H, cfg.L, cfg.E, cfg.I, cfg.K, cfg.Is
     TK = T * K
+    wb = EXPERT_WEIGHT_BYTES[experts]
     flops = dict(router_gemm=2 * T * H * E, fc1_shared_up=2 * T * H * (L + Is), expert_up=2 * TK * L * I,
                  expert_down=2 * TK * I * L, fc2_shared_down=2 * T * (L + Is) * H)
     bytes_ = dict(router_gemm=4 * E * H + 2 * T * H,
                   fc1_shared_up=2 * H * (L + Is) + 2 * T * H + 2 * T * (L + Is),
-                  expert_up=2 * n_touched * I * L + 2 * T * L + 2 * TK * I,
-                  expert_down=2 * n_touched * L * I + 2 * TK * I + 2 * TK * L,
+                  expert_up=int(wb * n_touched * I * L) + 2 * T * L + 2 * TK * I,
+                  expert_down=int(wb * n_touched * L * I) + 2 * TK * I + 2 * TK * L,
                   fc2_shared_down=2 * H * (L + Is) + 2 * T * (L + Is) + 2 * T * H)
     return flops, bytes_
 
 
-def cpu_baseline(d, cfg, idx_gpu, n_tokens: int):
-    """The oracle, as it stands, on n_tokens tokens of the same batch (host cores)."""
+def cpu_baseline(d, cfg, idx_gpu, n_tokens: int, experts_fmt: str = "bf16"):
+    """The oracle, as it stands, on n_tokens tokens of the same batch (host cores).
+    With MXFP8 experts the oracle runs on its own dequantised experts (quantised
+    untimed, like the host copies)."""
     import numpy as np
     import oracle
     import workloads as W
@@ -55,11 +62,21 @@ def cpu_baseline(d, cfg, idx_gpu, n_tokens: int):
     u = W.bf16_tensor_to_u16_numpy
     # host copies of the inputs, untimed
     need = sorted(set(idx_gpu[tokens].reshape(-1).tolist()))
-    experts = {e: (u(d["w_up"][e]), u(d["w_down"][e])) for e in need}
+
+    def host_expert(e):
+        up, down = u(d["w_up"][e]), u(d["w_down"][e])
+        if experts_fmt == "mxfp8":
+            def deq(bits):
+                v = oracle.dequantize_mxfp8(*oracle.quantize_mxfp8(oracle.bf16_bits_to_f64(bits)))
+                return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            up, down = deq(up), deq(down)
+        return up, down
+
+    experts = {e: host_expert(e) for e in need}
 
     def expert(e):
         if e not in experts:
-            experts[e] = (u(d["w_up"][e]), u(d["w_down"][e]))
+            experts[e] = host_expert(e)
         return experts[e]
 
     args = (u(d["x"][tokens]), d["w_router"].cpu().numpy(), d["corr_bias"].cpu().numpy(), u(d["w_fc1"]),
@@ -69,22 +86,23 @@ def cpu_baseline(d, cfg, idx_gpu, n_tokens: int):
     dt = time.perf_counter() - t0
     return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(tokens)} of the {cfg.T} tokens of the {cfg.name} batch (tokens are independent), "
-                      f"whole layer per token in float64 with bf16 rounding; {dt:.1f} s on "
+                      f"whole layer per token in float64 with bf16 rounding"
+                      f"{' (MXFP8 experts, dequantised)' if experts_fmt == 'mxfp8' else ''}; {dt:.1f} s on "
                       f"{os.cpu_count()} host cores, BLAS threads {threads}"}
 
 
-def graph_ms_per_step(M, d, weights, cfg, out, ws, steps: int) -> float:
-    """Capture one forward into a HIP graph (torch.cuda.CUDAGraph) and time its replays."""
+def graph_ms_per_step(fwd, steps: int) -> float:
+    """Capture one forward ``fwd()`` into a HIP graph (torch.cuda.CUDAGraph) and time its replays."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         for _ in range(2):
-            M.forward(d["x"], weights, cfg.K, cfg.routed_scaling, out=out, ws=ws)
+            fwd()
     torch.cuda.current_stream().wait_stream(side)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        M.forward(d["x"], weights, cfg.K, cfg.routed_scaling, out=out, ws=ws)
+        fwd()
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
@@ -102,6 +120,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ultra_prefill",
                     choices=["ultra_prefill", "ultra_decode64", "ultra_decode1", "nano", "super", "tiny"])
+    ap.add_argument("--experts", default="bf16", choices=["bf16", "mxfp8"],
+                    help="routed experts' weights: bf16, or MXFP8 (few-token workloads, T <= 64)")
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -128,17 +148,35 @@ def main():
     out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
     lay = M.workspace_layout(dims)
     stream = torch.cuda.current_stream()
+    if args.experts == "mxfp8":
+        if cfg.T > 64:
+            print("bench.py: MXFP8 experts are built for few-token forwards (T <= 64)", file=sys.stderr)
+            sys.exit(2)
+        mx = M.quantize_experts_mxfp8(weights)
+        run_w = {k: v for k, v in weights.items() if k not in ("w_up", "w_down")}
+
+        def fwd():
+            M.forward_mx(d["x"], run_w, mx, cfg.K, cfg.routed_scaling, out=out, ws=ws)
+
+        def fwd_prof(ev):
+            M.forward_mx_profiled(d["x"], run_w, mx, cfg.K, cfg.routed_scaling, ev, out=out, ws=ws, stream=stream)
+    else:
+        def fwd():
+            M.forward(d["x"], weights, cfg.K, cfg.routed_scaling, out=out, ws=ws)
+
+        def fwd_prof(ev):
+            M.forward_profiled(d["x"], weights, cfg.K, cfg.routed_scaling, ev, out=out, ws=ws, stream=stream)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        M.forward(d["x"], weights, cfg.K, cfg.routed_scaling, out=out, ws=ws)
+        fwd()
     torch.cuda.synchronize()
 
     evs = [M.PhaseEvents() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        M.forward_profiled(d["x"], weights, cfg.K, cfg.routed_scaling, evs[i], out=out, ws=ws, stream=stream)
+        fwd_prof(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
@@ -152,7 +190,7 @@ def main():
     # rows the grouped 256-row tiles cover (each expert's tail tile is padded)
     m_tiles = int(np.sum((np.diff(offsets) + 255) // 256))
     idx_gpu = ws[lay["idx"]:lay["idx"] + 4 * cfg.T * cfg.K].view(torch.int32).view(cfg.T, cfg.K).cpu().numpy()
-    flops, bytes_ = phase_work(cfg, n_touched)
+    flops, bytes_ = phase_work(cfg, n_touched, args.experts)
     total_flops = sum(flops.values())
     tokens_per_s = cfg.T / (ms_per_step / 1e3)
     tflops = total_flops / (ms_per_step / 1e3) / 1e12
@@ -166,7 +204,7 @@ def main():
         from sparse_moe_layer_correction_amd.profiling import kernel_source_hash
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        rec = tr.get(cfg.name, {}).get("phases", {}).get(dom)
+        rec = tr.get(cfg.name + ("" if args.experts == "bf16" else "_" + args.experts), {}).get("phases", {}).get(dom)
         family = "skinny" if cfg.T <= 64 else "gemm"
         if rec and rec.get("kernel_hash") == kernel_source_hash(family):
             traffic = rec["bytes_per_launch"]
@@ -184,7 +222,7 @@ def main():
                     "algorithmic_bytes_per_launch": bytes_[dom], "avg_launch_ms": round(phase_ms[dom], 4)}
 
     layer_bytes = 4 * cfg.E * cfg.H + 2 * 2 * cfg.H * cfg.L + 2 * 2 * cfg.H * cfg.Is + \
-        n_touched * 2 * 2 * cfg.I * cfg.L + 2 * 2 * cfg.T * cfg.H
+        int(n_touched * 2 * EXPERT_WEIGHT_BYTES[args.experts] * cfg.I * cfg.L) + 2 * 2 * cfg.T * cfg.H
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -199,7 +237,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded counter-based generator; random weights of the stated shapes)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "L": cfg.L, "E": cfg.E, "I": cfg.I,
-                   "K": cfg.K, "Is": cfg.Is, "routed_scaling": cfg.routed_scaling},
+                   "K": cfg.K, "Is": cfg.Is, "routed_scaling": cfg.routed_scaling, "experts": args.experts},
         "tflops": round(tflops, 2),
         "mfma_frac_layer": round(tflops / PEAK_BF16_TFLOPS, 4),
         "hbm_gbs_layer": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
@@ -214,11 +252,11 @@ def main():
     if cfg.T <= 64:
         # the same forward captured once into a HIP graph and replayed: what a
         # serving loop that replays captured decode steps pays per step
-        g_ms = graph_ms_per_step(M, d, weights, cfg, out, ws, args.steps)
+        g_ms = graph_ms_per_step(fwd, args.steps)
         result["graph_ms_per_step"] = round(g_ms, 4)
         result["graph_tokens_per_s"] = round(cfg.T / (g_ms / 1e3), 1)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, cfg, idx_gpu, args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(d, cfg, idx_gpu, args.cpu_tokens, args.experts)
     if args.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)

@@ -34,7 +34,7 @@ LIB_NAME = "libmoe_mi355x.so"
 EXPORTS = (
     "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
     "moe_workspace_bytes", "moe_workspace_layout", "moe_forward", "moe_forward_profiled", "moe_status_string",
-    "moe_abi_version",
+    "moe_abi_version", "moe_quantize_mxfp8", "moe_forward_mx", "moe_forward_mx_profiled",
 )
 
 # enum moe_phase of include/moe_api.h
@@ -55,6 +55,10 @@ class _Dims(ctypes.Structure):
 class _Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "corr_bias", "w_fc1", "w_up", "w_down", "w_fc2",
                                               "w_sh_up", "w_sh_down")]
+
+
+class _ExpertsMx(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_up", "w_up_scale", "w_down", "w_down_scale")]
 
 
 _LAYOUT_FIELDS = ("idx", "gate", "gap", "offsets", "row_token", "slot_row", "z", "h", "y", "y_lat", "hs", "total")
@@ -112,6 +116,10 @@ def load_library(path: Optional[str] = None):
                                        ctypes.POINTER(ctypes.c_void_p), i32]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_abi_version": (i32, []),
+        "moe_quantize_mxfp8": (i32, [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]),
+        "moe_forward_mx": (i32, [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_ExpertsMx), vp, vp, vp, sz, vp]),
+        "moe_forward_mx_profiled": (i32, [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_ExpertsMx), vp, vp, vp,
+                                          sz, vp, ctypes.POINTER(ctypes.c_void_p), i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -251,17 +259,102 @@ def permute(topk_idx, E: int, src=None, *, ws=None, stream=None):
 _WEIGHT_SPECS = ("w_router", "corr_bias", "w_fc1", "w_up", "w_down", "w_fc2", "w_sh_up", "w_sh_down")
 
 
-def _weight_struct(dims: MoEDims, w: Dict, dev):
+def _weight_struct(dims: MoEDims, w: Dict, dev, experts: bool = True):
+    """experts=False: the bf16 expert weights are not needed (MXFP8 experts given apart)."""
     torch = _torch()
     H, L, E, I, Is = dims.H, dims.L, dims.E, dims.I, dims.Is
     shapes = {"w_router": ((E, H), torch.float32), "corr_bias": ((E,), torch.float32),
               "w_fc1": ((L, H), torch.bfloat16), "w_up": ((E, I, L), torch.bfloat16),
               "w_down": ((E, L, I), torch.bfloat16), "w_fc2": ((H, L), torch.bfloat16),
               "w_sh_up": ((Is, H), torch.bfloat16), "w_sh_down": ((H, Is), torch.bfloat16)}
-    for n in _WEIGHT_SPECS:
+    names = [n for n in _WEIGHT_SPECS if experts or n not in ("w_up", "w_down")]
+    for n in names:
         shp, dt = shapes[n]
         _need(w[n], n, dt, shp, dev)
-    return _Weights(*[_ptr(w[n]) for n in _WEIGHT_SPECS])
+    return _Weights(*[_ptr(w[n]) if n in names else None for n in _WEIGHT_SPECS])
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 expert weights
+# ----------------------------------------------------------------------------
+
+def quantize_mxfp8(w, *, stream=None):
+    """moe_quantize_mxfp8: bf16 [..., C] (C a multiple of 32) -> (codes uint8 [..., C],
+    scales uint8 [..., C/32])."""
+    torch = _torch()
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.bfloat16 or not w.is_cuda or not w.is_contiguous():
+        raise TypeError("w must be a contiguous bf16 CUDA tensor")
+    C = w.shape[-1]
+    rows = w.numel() // C
+    codes = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(w.shape[:-1] + (C // 32,), dtype=torch.uint8, device=w.device)
+    _check(load_library().moe_quantize_mxfp8(_ptr(w), rows, C, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def quantize_experts_mxfp8(weights: Dict, *, stream=None) -> Dict:
+    """The routed experts' weights of ``weights`` as MXFP8 (keys of moe_experts_mx)."""
+    up, up_s = quantize_mxfp8(weights["w_up"], stream=stream)
+    down, down_s = quantize_mxfp8(weights["w_down"], stream=stream)
+    return {"w_up": up, "w_up_scale": up_s, "w_down": down, "w_down_scale": down_s}
+
+
+def _mx_struct(dims: MoEDims, mx: Dict, dev):
+    torch = _torch()
+    E, L, I = dims.E, dims.L, dims.I
+    shapes = {"w_up": (E, I, L), "w_up_scale": (E, I, L // 32), "w_down": (E, L, I), "w_down_scale": (E, L, I // 32)}
+    for n, shp in shapes.items():
+        _need(mx[n], n, torch.uint8, shp, dev)
+    return _ExpertsMx(*[_ptr(mx[n]) for n in ("w_up", "w_up_scale", "w_down", "w_down_scale")])
+
+
+def dims_from_mx(x, weights: Dict, mx: Dict, K: int, routed_scaling: float = 5.0, n_group: int = 1,
+                 topk_group: int = 1) -> MoEDims:
+    T, H = x.shape
+    E, I, L = mx["w_up"].shape
+    Is = weights["w_sh_up"].shape[0]
+    return MoEDims(T, H, L, E, I, K, Is, routed_scaling, n_group, topk_group)
+
+
+def forward_mx(x, weights: Dict, mx: Dict, K: int, routed_scaling: float = 5.0, *, out=None, ws=None,
+               stream=None, n_group: int = 1, topk_group: int = 1):
+    """moe_forward_mx: the forward with MXFP8 expert weights ``mx`` (T <= 64)."""
+    torch = _torch()
+    dims = dims_from_mx(x, weights, mx, K, routed_scaling, n_group, topk_group)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (dims.T, dims.H), dev)
+    wstruct = _weight_struct(dims, weights, dev, experts=False)
+    mstruct = _mx_struct(dims, mx, dev)
+    d = dims.c()
+    lib = load_library()
+    if out is None:
+        out = torch.empty(dims.T, dims.H, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (dims.T, dims.H), dev)
+    nbytes = lib.moe_workspace_bytes(ctypes.byref(d))
+    if nbytes == 0:
+        _check(lib.moe_forward_mx(ctypes.byref(d), ctypes.byref(wstruct), ctypes.byref(mstruct), None, None, None, 0,
+                                  None))
+    w = _workspace(nbytes, dev, ws)
+    _check(lib.moe_forward_mx(ctypes.byref(d), ctypes.byref(wstruct), ctypes.byref(mstruct), _ptr(x), _ptr(out),
+                              _ptr(w), w.numel() * w.element_size(), _stream(stream)))
+    return out
+
+
+def forward_mx_profiled(x, weights: Dict, mx: Dict, K: int, routed_scaling: float, events: "PhaseEvents", *, out,
+                        ws, stream=None):
+    """moe_forward_mx_profiled: forward_mx with an event recorded before each phase."""
+    torch = _torch()
+    dims = dims_from_mx(x, weights, mx, K, routed_scaling)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (dims.T, dims.H), dev)
+    _need(out, "out", torch.bfloat16, (dims.T, dims.H), dev)
+    wstruct = _weight_struct(dims, weights, dev, experts=False)
+    mstruct = _mx_struct(dims, mx, dev)
+    d = dims.c()
+    _check(load_library().moe_forward_mx_profiled(ctypes.byref(d), ctypes.byref(wstruct), ctypes.byref(mstruct),
+                                                  _ptr(x), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                                  _stream(stream), events.events, events.n))
+    return out
 
 
 def dims_from(x, weights: Dict, K: int, routed_scaling: float = 5.0, n_group: int = 1,

@@ -38,8 +38,15 @@ struct SkinnyProblem {
   int epi;
   int ksplit;                // dense: K split over this many waves per slab
   float* partial;            // [ksplit, M, N] fp32 when ksplit > 1, else null
+  // MXFP8 weights (grouped products, one K segment): when set, B comes from
+  // E4M3 codes [.., N, K] (b_estride apart per expert, row length seg[0].ldb)
+  // and E8M0 scales, one per 32 k; seg[0].B is then unused
+  const uint8_t* mx_codes;
+  const uint8_t* mx_scales;
 };
 hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st);
+hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t st);
 int skinny_slabs_per_wave(const SkinnyProblem& P);
 
 struct PermuteScratch {

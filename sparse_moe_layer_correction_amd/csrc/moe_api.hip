@@ -26,14 +26,14 @@ constexpr int kSkinnyMaxT = 64;
 constexpr int kSkinnyTargetWaves = 2048;
 
 int skinny_ksplit(int N, int K, int M) {
-  if (N <= 0 || K < 32) return 1;
+  if (N <= 0 || K < 64) return 1;
   const int width = M > 16 ? 64 : 16;      // columns per wave (see skinny_slabs_per_wave)
   const int slabs = (N + width - 1) / width;
   int ks = (kSkinnyTargetWaves + slabs - 1) / slabs;
   // the fp32 partials are written once and read once: 8*ks*M*N bytes against
   // 2*N*K bytes of weights; keep them within a quarter of the weight traffic
   const int cap = std::max(1, K / (16 * std::max(M, 1)));
-  ks = std::max(1, std::min(std::min(ks, cap), K / 32));
+  ks = std::max(1, std::min(std::min(ks, cap), K / 64));   // whole 64-deep steps per split
   return ks;
 }
 
@@ -354,13 +354,20 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* s
 
 namespace {
 
+// mx: MXFP8 expert weights (then w->w_up / w->w_down are not read), or null.
 int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
-                 size_t ws_bytes, hipStream_t stream, const Marks& mk) {
+                 size_t ws_bytes, hipStream_t stream, const Marks& mk, const moe_experts_mx* mx = nullptr) {
   int st;
   if (!dims_ok(dims, &st)) return st;
-  if (!w || !x || !out || !w->w_router || !w->corr_bias || !w->w_fc1 || !w->w_up || !w->w_down || !w->w_fc2 ||
-      !w->w_sh_up || !w->w_sh_down)
+  if (!w || !x || !out || !w->w_router || !w->corr_bias || !w->w_fc1 || !w->w_fc2 || !w->w_sh_up || !w->w_sh_down)
     return MOE_ERR_INVALID;
+  if (mx != nullptr) {
+    if (!mx->w_up || !mx->w_up_scale || !mx->w_down || !mx->w_down_scale) return MOE_ERR_INVALID;
+    if (((uintptr_t)mx->w_up | (uintptr_t)mx->w_down) & 15) return MOE_ERR_INVALID;
+    if (dims->T > kSkinnyMaxT) return MOE_ERR_UNSUPPORTED;   // the tiled expert products take bf16 only
+  } else if (!w->w_up || !w->w_down) {
+    return MOE_ERR_INVALID;
+  }
   const moe_dims& d = *dims;
   const Layout l = make_layout(d);
   if (!ws_ok(ws, ws_bytes, l.total)) return MOE_ERR_WORKSPACE;
@@ -415,7 +422,8 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     if (mk.mark(MOE_PHASE_EXPERT_UP) != hipSuccess) return MOE_ERR_HIP;
     SkinnyProblem P = skinny_grouped(std::min(d.E, d.T * d.K), ps, d.I, offsets, row_token, I * L, h, I,
                                      EPI_RELU2_BF16);
-    add_seg(P, z, L, w->w_up, L, d.L);
+    add_seg(P, z, L, mx ? nullptr : w->w_up, L, d.L);
+    if (mx) { P.mx_codes = mx->w_up; P.mx_scales = mx->w_up_scale; }
     if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
   } else {
     const TileShape ts = tile_shape(kGroupedCfg);
@@ -446,7 +454,8 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   if (skinny) {
     if (mk.mark(MOE_PHASE_EXPERT_DOWN) != hipSuccess) return MOE_ERR_HIP;
     SkinnyProblem P = skinny_grouped(std::min(d.E, d.T * d.K), ps, d.L, offsets, nullptr, L * I, y, L, EPI_BF16);
-    add_seg(P, h, I, w->w_down, I, d.I);
+    add_seg(P, h, I, mx ? nullptr : w->w_down, I, d.I);
+    if (mx) { P.mx_codes = mx->w_down; P.mx_scales = mx->w_down_scale; }
     if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
   } else {
     const TileShape ts = tile_shape(kGroupedCfg);
@@ -513,6 +522,29 @@ int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint1
   for (int i = 0; i <= MOE_N_PHASES; ++i)
     if (events[i] == nullptr) return MOE_ERR_INVALID;
   return forward_impl(dims, w, x, out, ws, ws_bytes, stream, Marks{events, stream});
+}
+
+int moe_forward_mx(const moe_dims* dims, const moe_weights* w, const moe_experts_mx* mx, const uint16_t* x,
+                   uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (mx == nullptr) return MOE_ERR_INVALID;
+  return forward_impl(dims, w, x, out, ws, ws_bytes, stream, Marks{nullptr, stream}, mx);
+}
+
+int moe_forward_mx_profiled(const moe_dims* dims, const moe_weights* w, const moe_experts_mx* mx, const uint16_t* x,
+                            uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                            int n_events) {
+  if (mx == nullptr || events == nullptr || n_events < MOE_N_PHASES + 1) return MOE_ERR_INVALID;
+  for (int i = 0; i < MOE_N_PHASES + 1; ++i)
+    if (events[i] == nullptr) return MOE_ERR_INVALID;
+  return forward_impl(dims, w, x, out, ws, ws_bytes, stream, Marks{events, stream}, mx);
+}
+
+int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream) {
+  if (rows <= 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID;
+  if (src == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID;
+  if (((uintptr_t)src | (uintptr_t)codes) & 15) return MOE_ERR_INVALID;
+  return hip_status(launch_mxfp8_quantize(src, rows * (cols / 32), codes, scales, stream));
 }
 
 }  // extern "C"

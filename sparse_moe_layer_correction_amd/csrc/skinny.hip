@@ -16,19 +16,53 @@
 // KSPLIT waves per column block; each writes its fp32 partial and skinny_reduce sums
 // the partials in a fixed order and applies the epilogue, so results do not
 // depend on timing. Grouped products (experts) need no split: a slab of one
-// expert covers its rows, and there are E x N/16 slabs.
+// expert covers its rows, and there are E x N/16 slabs. Their weights may also
+// come as MXFP8 (E4M3 codes with a power-of-two scale per 32 k), decoded to
+// bf16 in registers on the way to the MFMA: half the bytes of bf16 weights.
 #include "kernels.h"
 
 namespace moe {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
-int skinny_slabs_per_wave(const SkinnyProblem& P) { return (P.offsets == nullptr && P.M > 16) ? 4 : 1; }
+// 8 E4M3 codes (k order, lowest byte first) times the block scale 2^(s - 127)
+// as one bf16 MFMA operand: v_cvt_scalef32_pk_bf16_fp8 decodes two codes and
+// scales them; the products are bf16 values, so nothing is rounded.
+__device__ __forceinline__ u32x4 mx_decode8(u32x2 c, uint32_t s) {
+  const float sc = __uint_as_float(s == 0 ? 0x00400000u : (s << 23));
+  const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false);
+  const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true);
+  const bf16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false);
+  const bf16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true);
+  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
+               __builtin_bit_cast(uint32_t, p3)};
+}
 
-// MT m-tiles of 16 rows and NS slabs of 16 columns per wave: per 32-deep k step
-// the wave loads NS weight fragments and MT activation fragments and issues
-// MT*NS MFMAs, so the activations are read once per NS weight fragments.
-template <int MT, int NS, int UNROLL>
+// weight bytes each lane keeps in flight (the loop unroll follows from it)
+#ifndef MOE_SKINNY_INFLIGHT
+#define MOE_SKINNY_INFLIGHT 128
+#endif
+// grouped products take 4 slabs per wave (activations reused 4x) when that
+// still leaves this many waves
+#ifndef MOE_GROUPED_WIDE_WAVES
+#define MOE_GROUPED_WIDE_WAVES (1 << 30)
+#endif
+
+int skinny_slabs_per_wave(const SkinnyProblem& P) {
+  if (P.offsets == nullptr) return P.M > 16 ? 4 : 1;
+  return (int64_t)P.groups * ((P.N + 63) / 64) >= MOE_GROUPED_WIDE_WAVES ? 4 : 1;
+}
+
+// MT m-tiles of 16 rows and NS slabs of 16 columns per wave. The k axis goes
+// in 64-deep steps of two 16x16x32 MFMAs; in each step lane group g = lane/16
+// holds k = 16g .. 16g+15 of the step (the first MFMA takes its low 8, the
+// second its high 8), so a lane's weights of a step are 16 consecutive
+// elements: two 16-byte loads of bf16, or one 16-byte load of MXFP8 codes plus
+// the one scale byte they share. The activations are loaded in the same k
+// order, so the products are unchanged; per step the wave issues MT*NS*2
+// MFMAs and reads the activations once per NS weight fragments.
+template <int MT, int NS, int UNROLL, bool MX>
 __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first, int rows, int row0,
                                             const int32_t* gather, int64_t b_base, int k_begin, int k_end,
                                             int out_row0, float* partial, int lane, int epi) {
@@ -42,12 +76,19 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
   int nrow[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) nrow[j] = min(n_first + j * 16 + (lane & 15), P.Nb - 1);
-  const int kl = (lane >> 4) * 8;          // this lane's 8 k values within a 32-wide step
+  const int kl = (lane >> 4) * 16;         // this lane's 16 k values within a 64-wide step
   f32x4v acc[NS][MT];
 #pragma unroll
   for (int j = 0; j < NS; ++j)
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[j][t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+  // what one lane loads for one slab in one step: bf16 weights (two fragments)
+  // or MXFP8 codes (decoded at use) and their block scale
+  struct BRaw {
+    u32x4 w0, w1;
+    uint32_t s;
+  };
 
   // walk the K segments; k indices are global over the concatenated segments
   int seg_k0 = 0;
@@ -56,45 +97,78 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
     const int lo = max(k_begin, seg_k0), hi = min(k_end, seg_k0 + S.K);
     if (lo < hi) {
       const uint16_t* bp[NS];
+      const uint8_t* cp[NS];                 // MX: codes and the block scale of this lane's k
+      const uint8_t* sp[NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) bp[j] = S.B + b_base + (int64_t)nrow[j] * S.ldb + (lo - seg_k0) + kl;
+      for (int j = 0; j < NS; ++j) {
+        if constexpr (MX) {
+          cp[j] = P.mx_codes + b_base + (int64_t)nrow[j] * S.ldb + (lo - seg_k0) + kl;
+          sp[j] = P.mx_scales + b_base / 32 + (int64_t)nrow[j] * (S.ldb / 32) + (lo - seg_k0 + kl) / 32;
+        } else {
+          bp[j] = S.B + b_base + (int64_t)nrow[j] * S.ldb + (lo - seg_k0) + kl;
+        }
+      }
+      auto load_b = [&](int j, int st) -> BRaw {
+        BRaw r;
+        if constexpr (MX) {
+          r.w0 = *reinterpret_cast<const u32x4*>(cp[j] + st * 64);
+          r.s = sp[j][st * 2];
+        } else {
+          r.w0 = *reinterpret_cast<const u32x4*>(bp[j] + st * 64);
+          r.w1 = *reinterpret_cast<const u32x4*>(bp[j] + st * 64 + 8);
+        }
+        return r;
+      };
       const uint16_t* ap[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) ap[t] = S.A + arow[t] * S.lda + (lo - seg_k0) + kl;
-      const int nsteps = (hi - lo) / 32;
+      auto mfma_step = [&](const BRaw (&b)[NS], const u32x4 (&a0)[MT], const u32x4 (&a1)[MT]) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          u32x4 w0 = b[j].w0, w1 = b[j].w1;
+          if constexpr (MX) {
+            w1 = mx_decode8(u32x2{b[j].w0.z, b[j].w0.w}, b[j].s);
+            w0 = mx_decode8(u32x2{b[j].w0.x, b[j].w0.y}, b[j].s);
+          }
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0),
+                                                                __builtin_bit_cast(bf16x8, a0[t]), acc[j][t], 0, 0, 0);
+            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1),
+                                                                __builtin_bit_cast(bf16x8, a1[t]), acc[j][t], 0, 0, 0);
+          }
+        }
+      };
+      const int nsteps = (hi - lo) / 64;
       int st = 0;
       for (; st + UNROLL <= nsteps; st += UNROLL) {
-        u32x4 bv[UNROLL][NS], av[UNROLL][MT];
+        BRaw bv[UNROLL][NS];
+        u32x4 a0[UNROLL][MT], a1[UNROLL][MT];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-          for (int j = 0; j < NS; ++j) bv[u][j] = *reinterpret_cast<const u32x4*>(bp[j] + (st + u) * 32);
+          for (int j = 0; j < NS; ++j) bv[u][j] = load_b(j, st + u);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-          for (int t = 0; t < MT; ++t) av[u][t] = *reinterpret_cast<const u32x4*>(ap[t] + (st + u) * 32);
+          for (int t = 0; t < MT; ++t) {
+            a0[u][t] = *reinterpret_cast<const u32x4*>(ap[t] + (st + u) * 64);
+            a1[u][t] = *reinterpret_cast<const u32x4*>(ap[t] + (st + u) * 64 + 8);
+          }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-          for (int j = 0; j < NS; ++j)
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-              acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bv[u][j]),
-                                                                  __builtin_bit_cast(bf16x8, av[u][t]), acc[j][t], 0, 0,
-                                                                  0);
+        for (int u = 0; u < UNROLL; ++u) mfma_step(bv[u], a0[u], a1[u]);
       }
       for (; st < nsteps; ++st) {
-        u32x4 bv[NS], av[MT];
+        BRaw bv[NS];
+        u32x4 a0[MT], a1[MT];
 #pragma unroll
-        for (int j = 0; j < NS; ++j) bv[j] = *reinterpret_cast<const u32x4*>(bp[j] + st * 32);
+        for (int j = 0; j < NS; ++j) bv[j] = load_b(j, st);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) av[t] = *reinterpret_cast<const u32x4*>(ap[t] + st * 32);
-#pragma unroll
-        for (int j = 0; j < NS; ++j)
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bv[j]),
-                                                                __builtin_bit_cast(bf16x8, av[t]), acc[j][t], 0, 0, 0);
+        for (int t = 0; t < MT; ++t) {
+          a0[t] = *reinterpret_cast<const u32x4*>(ap[t] + st * 64);
+          a1[t] = *reinterpret_cast<const u32x4*>(ap[t] + st * 64 + 8);
+        }
+        mfma_step(bv, a0, a1);
       }
     }
     seg_k0 += S.K;
@@ -129,7 +203,12 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
 // GROUPED_EPI: -1 for dense products (epilogue from the problem), else the
 // fixed epilogue of a grouped expert product (which also names up and down
 // apart in profiles).
-template <int NSB, int GROUPED_EPI>
+constexpr int unroll_steps(int mt, int nsb, bool mx) {
+  const int u = MOE_SKINNY_INFLIGHT / (nsb * mt * (mx ? 16 : 32));
+  return u > 0 ? u : 1;
+}
+
+template <int NSB, int GROUPED_EPI, bool MX = false>
 __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -153,9 +232,9 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
 
   int ktot = 0;
   for (int s = 0; s < P.nseg; ++s) ktot += P.seg[s].K;
-  const int ksteps = ktot / 32;
-  const int k_begin = (int)((int64_t)ksteps * ks / P.ksplit) * 32;
-  const int k_end = (int)((int64_t)ksteps * (ks + 1) / P.ksplit) * 32;
+  const int ksteps = ktot / 64;
+  const int k_begin = (int)((int64_t)ksteps * ks / P.ksplit) * 64;
+  const int k_end = (int)((int64_t)ksteps * (ks + 1) / P.ksplit) * 64;
   float* partial = P.partial ? P.partial + (int64_t)ks * P.M * P.N : nullptr;
   const int n_first = blk * 16 * NSB;
   const int epi = GROUPED_EPI >= 0 ? GROUPED_EPI : P.epi;
@@ -163,15 +242,16 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
   // up to 64 rows in registers per pass; more rows take further passes
   for (int r0 = 0; r0 < rows; r0 += 64) {
     const int rr = min(64, rows - r0);
+    // steps in flight per lane: about 128 bytes of weights (MXFP8 codes are half as large)
     if (rr <= 16)
-      skinny_tile<1, NSB, 8 / NSB>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end, row0 + r0, partial,
-                                    lane, epi);
+      skinny_tile<1, NSB, unroll_steps(1, NSB, MX), MX>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
+                                                       row0 + r0, partial, lane, epi);
     else if (rr <= 32)
-      skinny_tile<2, NSB, (4 / NSB > 0 ? 4 / NSB : 1)>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
-                                                        row0 + r0, partial, lane, epi);
+      skinny_tile<2, NSB, unroll_steps(2, NSB, MX), MX>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
+                                                       row0 + r0, partial, lane, epi);
     else
-      skinny_tile<4, NSB, (2 / NSB > 0 ? 2 / NSB : 1)>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
-                                                        row0 + r0, partial, lane, epi);
+      skinny_tile<4, NSB, unroll_steps(4, NSB, MX), MX>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
+                                                       row0 + r0, partial, lane, epi);
   }
 }
 
@@ -203,10 +283,25 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
   const int64_t tasks = (int64_t)P.groups * nblocks * P.ksplit;
   if (tasks <= 0) return hipSuccess;
   const dim3 grid((unsigned)((tasks + 3) / 4)), block(256);
-  if (nsb == 4) hipLaunchKernelGGL((skinny_kernel<4, -1>), grid, block, 0, st, P);
-  else if (P.offsets == nullptr) hipLaunchKernelGGL((skinny_kernel<1, -1>), grid, block, 0, st, P);
-  else if (P.epi == EPI_RELU2_BF16) hipLaunchKernelGGL((skinny_kernel<1, EPI_RELU2_BF16>), grid, block, 0, st, P);
-  else hipLaunchKernelGGL((skinny_kernel<1, EPI_BF16>), grid, block, 0, st, P);
+  if (P.offsets == nullptr) {
+    if (P.mx_codes != nullptr) return hipErrorInvalidValue;     // MXFP8 weights: grouped products only
+    if (nsb == 4) hipLaunchKernelGGL((skinny_kernel<4, -1>), grid, block, 0, st, P);
+    else hipLaunchKernelGGL((skinny_kernel<1, -1>), grid, block, 0, st, P);
+  } else {
+    if (P.mx_codes != nullptr && P.nseg != 1) return hipErrorInvalidValue;
+    const bool relu2 = P.epi == EPI_RELU2_BF16, mx = P.mx_codes != nullptr;
+#define MOE_GROUPED(NS)                                                                                       \
+  if (relu2 && mx) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16, true>), grid, block, 0, st, P);     \
+  else if (relu2) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16, false>), grid, block, 0, st, P);     \
+  else if (mx) hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16, true>), grid, block, 0, st, P);               \
+  else hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16, false>), grid, block, 0, st, P);
+    if (nsb == 4) {
+      MOE_GROUPED(4)
+    } else {
+      MOE_GROUPED(1)
+    }
+#undef MOE_GROUPED
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.partial == nullptr) return e;
   const int64_t total = (int64_t)P.M * P.N;

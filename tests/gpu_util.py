@@ -73,15 +73,20 @@ def oracle_route(d, tokens=None, n_group=1, topk_group=1):
                         cfg.K, cfg.routed_scaling, n_group=n_group, topk_group=topk_group)
 
 
-def oracle_forward_tokens(d, tokens, idx_override=None, mirror=True, keep=False, n_group=1, topk_group=1):
-    """The oracle on a subset of tokens (tokens are independent), experts copied on demand."""
+def oracle_forward_tokens(d, tokens, idx_override=None, mirror=True, keep=False, n_group=1, topk_group=1,
+                          expert=None):
+    """The oracle on a subset of tokens (tokens are independent), experts copied on
+    demand (or given by ``expert(e) -> (w_up bits, w_down bits)``)."""
     cfg = d["cfg"]
     cache = {}
 
-    def expert(e):
+    def host_expert(e):
         if e not in cache:
             cache[e] = (u16(d["w_up"][e]), u16(d["w_down"][e]))
         return cache[e]
+
+    if expert is None:
+        expert = host_expert
 
     return oracle.forward(u16(d["x"][tokens]), host_f32(d["w_router"]), host_f32(d["corr_bias"]),
                           u16(d["w_fc1"]), u16(d["w_fc2"]), u16(d["w_sh_up"]), u16(d["w_sh_down"]),

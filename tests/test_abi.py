@@ -147,3 +147,29 @@ def test_expert_groups_accepted(lib, ng, tg):
                   n_group=ng, topk_group=tg)
     assert lib.moe_workspace_bytes(_d(d)) > 0
     assert lib.moe_route_workspace_bytes(_d(d)) > 0
+
+
+def test_mxfp8_entry_points_validate_before_any_launch(lib):
+    q = lib.moe_quantize_mxfp8
+    assert q(256, 4, 48, 256, 256, None) == -1       # cols not a multiple of 32
+    assert q(256, 0, 64, 256, 256, None) == -1       # no rows
+    assert q(None, 4, 64, 256, 256, None) == -1
+    assert q(256, 4, 64, 256, None, None) == -1
+    assert q(264, 4, 64, 256, 256, None) == -1       # misaligned source
+    assert q(256, 4, 64, 264, 256, None) == -1       # misaligned codes
+    d = _d(TINY)
+    need = lib.moe_workspace_bytes(d)
+    w = M._Weights(*([256] * 3 + [0, 0] + [256] * 3))     # bf16 experts not needed with mx
+    mx = M._ExpertsMx(256, 256, 256, 256)
+    f = lib.moe_forward_mx
+    assert f(d, ctypes.byref(w), None, 256, 256, 256, need, None) == -1
+    assert f(d, ctypes.byref(w), ctypes.byref(M._ExpertsMx(256, 0, 256, 256)), 256, 256, 256, need, None) == -1
+    assert f(d, ctypes.byref(w), ctypes.byref(M._ExpertsMx(264, 256, 256, 256)), 256, 256, 256, need, None) == -1
+    assert f(d, ctypes.byref(w), ctypes.byref(mx), 256, 256, 256, need - 1, None) == -3
+    big = M.MoEDims(65, TINY.H, TINY.L, TINY.E, TINY.I, TINY.K, TINY.Is)
+    assert f(_d(big), ctypes.byref(w), ctypes.byref(mx), 256, 256, 256, lib.moe_workspace_bytes(_d(big)),
+             None) == -2                              # the tiled products read bf16 experts only
+    # the bf16 entry point still needs its expert weights
+    assert lib.moe_forward(d, ctypes.byref(w), 256, 256, 256, need, None) == -1
+    ev = (ctypes.c_void_p * 8)()
+    assert lib.moe_forward_mx_profiled(d, ctypes.byref(w), ctypes.byref(mx), 256, 256, 256, need, None, ev, 8) == -1
