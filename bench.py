@@ -113,6 +113,45 @@ def graph_ms_per_step(fwd, steps: int) -> float:
     return 1e3 * (time.perf_counter() - t0) / steps
 
 
+def block_timing(M, d, weights, cfg, args, mx, ws, lay):
+    """The block step (RMSNorm, the layer, the fused residual add) and its two
+    extra kernels, each timed with HIP events on the stream it runs on."""
+    import torch
+    gamma = (1.0 + 0.25 * torch.randn(cfg.H, generator=torch.Generator().manual_seed(7))).to(torch.bfloat16).cuda()
+    dims = M.dims_from(d["x"], weights, cfg.K, cfg.routed_scaling)
+    bws = torch.empty(M.block_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["x"])
+    w = weights if mx is None else {k: v for k, v in weights.items() if k not in ("w_up", "w_down")}
+    step = lambda: M.block_forward(d["x"], w, gamma, cfg.K, cfg.routed_scaling, mx=mx, out=out, ws=bws)
+    y = torch.empty_like(d["x"])
+    norm = lambda: M.rmsnorm(d["x"], gamma, out=y)
+    offsets = ws[lay["offsets"]:lay["offsets"] + 4 * (cfg.E + 1)].view(torch.int32)
+    bias = d["corr_bias"].clone()
+    upd = lambda: M.bias_update(offsets, bias, 1e-3)
+
+    def timed(fn, n):
+        for _ in range(max(2, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    blk_ms = timed(step, args.steps)
+    norm_ms = timed(norm, max(args.steps, 20))
+    upd_ms = timed(upd, 50)
+    norm_bytes = 2 * 2 * cfg.T * cfg.H + 2 * cfg.H
+    return {"ms_per_step": round(blk_ms, 4), "tokens_per_s": round(cfg.T / (blk_ms / 1e3), 1),
+            "rmsnorm": {"bound": "hbm", "avg_launch_ms": round(norm_ms, 4), "algorithmic_bytes": norm_bytes,
+                        "achieved": round(norm_bytes / (norm_ms / 1e3) / 1e9, 1), "unit": "GB/s",
+                        "frac": round(norm_bytes / (norm_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "bias_update_us": round(upd_ms * 1e3, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +161,8 @@ def main():
                     choices=["ultra_prefill", "ultra_decode64", "ultra_decode1", "nano", "super", "tiny"])
     ap.add_argument("--experts", default="bf16", choices=["bf16", "mxfp8"],
                     help="routed experts' weights: bf16, or MXFP8 (few-token workloads, T <= 64)")
+    ap.add_argument("--block", action="store_true",
+                    help="also time the block around the layer: RMSNorm + layer + residual, and the bias update")
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -255,6 +296,8 @@ def main():
         g_ms = graph_ms_per_step(fwd, args.steps)
         result["graph_ms_per_step"] = round(g_ms, 4)
         result["graph_tokens_per_s"] = round(cfg.T / (g_ms / 1e3), 1)
+    if args.block:
+        result["block"] = block_timing(M, d, weights, cfg, args, mx if args.experts == "mxfp8" else None, ws, lay)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, cfg, idx_gpu, args.cpu_tokens, args.experts)
     if args.calibrate_copy:

@@ -219,6 +219,51 @@ int moe_forward_mx_profiled(const moe_dims* dims, const moe_weights* w, const mo
                             const uint16_t* x, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream,
                             hipEvent_t* events, int n_events);
 
+/* ---- the layer's neighbours: pre-norm, residual, bias update ------------ */
+
+/* Pre-norm RMSNorm (the QA page, CH2 Q2.8): per row t of x,
+ *   y[t] = bf16( gamma * bf16( x[t] * rsqrt(mean_k x[t,k]^2 + eps) ) )
+ * x, y device [T, H] bf16; gamma device [H] bf16 (the learned weight). The
+ * page upcasts to fp32; here the mean, the scale and both products are
+ * float64 and each rounding is one round-to-nearest-even to bf16, so every
+ * output is the unique value of the definition (torch's fp32 execution of the
+ * page's code can differ on rare elements by one bf16 step). x, gamma and y
+ * must be 16-byte aligned; y may equal x. MOE_ERR_INVALID for null or
+ * misaligned pointers, T <= 0, H not a positive multiple of 8, or eps
+ * negative / not finite. Asynchronous on `stream`. */
+int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, int64_t T, int32_t H, float eps, uint16_t* y,
+                hipStream_t stream);
+
+/* Workspace of moe_block_forward: moe_workspace_bytes plus the normed rows
+ * (T * H bf16). 0 for invalid dims. */
+size_t moe_block_workspace_bytes(const moe_dims* dims);
+
+/* The MoE block (the QA page, CH2 Q2.1 point 3: each mixer sits inside
+ * Pre-Norm + Residual; the block sketch of the 2kiu.com hybrid Mamba/MoE
+ * walkthrough: residual = x, x = norm(x), x = residual + MoE(x)):
+ *   out = bf16( x + moe_forward(moe_rmsnorm(x, gamma, eps)) )
+ * The norm writes the normed rows into the workspace (after the layer's own
+ * scratch; its moe_ws_layout offsets are unchanged) and the residual add runs
+ * in the epilogue of the final product: fc2 + shared down are rounded to bf16,
+ * added to x in fp32 and rounded once more. mx: NULL for the bf16 experts of
+ * `w`, else MXFP8 experts as for moe_forward_mx (T <= 64). out may equal x
+ * (every element of x is read before the same element of out is written).
+ * Errors as moe_forward, plus MOE_ERR_INVALID for a null or misaligned gamma
+ * or x, or a bad eps; MOE_ERR_WORKSPACE below moe_block_workspace_bytes. */
+int moe_block_forward(const moe_dims* dims, const moe_weights* w, const moe_experts_mx* mx, const uint16_t* gamma,
+                      float eps, const uint16_t* x, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Auxiliary-loss-free load balancing (the QA page, CH5 Q5.3): with load_i the
+ * slots routed to expert i (offsets[i+1] - offsets[i]) and the mean load
+ * offsets[E] / E,
+ *   corr_bias[i] <- corr_bias[i] - eta * (load_i - mean load)
+ * evaluated in float64 without fused multiply-adds and rounded once to fp32.
+ * offsets device [E+1] int32: the expert offsets of moe_permute, or those a
+ * forward left in its workspace (moe_ws_layout.offsets). corr_bias device [E]
+ * fp32, updated in place. MOE_ERR_INVALID for null pointers, E <= 0 or a
+ * non-finite eta. Asynchronous on `stream`. */
+int moe_bias_update(const int32_t* offsets, int32_t E, float eta, float* corr_bias, hipStream_t stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(int status);
 

@@ -35,6 +35,7 @@ EXPORTS = (
     "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
     "moe_workspace_bytes", "moe_workspace_layout", "moe_forward", "moe_forward_profiled", "moe_status_string",
     "moe_abi_version", "moe_quantize_mxfp8", "moe_forward_mx", "moe_forward_mx_profiled",
+    "moe_rmsnorm", "moe_block_workspace_bytes", "moe_block_forward", "moe_bias_update",
 )
 
 # enum moe_phase of include/moe_api.h
@@ -120,6 +121,11 @@ def load_library(path: Optional[str] = None):
         "moe_forward_mx": (i32, [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_ExpertsMx), vp, vp, vp, sz, vp]),
         "moe_forward_mx_profiled": (i32, [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_ExpertsMx), vp, vp, vp,
                                           sz, vp, ctypes.POINTER(ctypes.c_void_p), i32]),
+        "moe_rmsnorm": (i32, [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, vp, vp]),
+        "moe_block_workspace_bytes": (sz, [dims_p]),
+        "moe_block_forward": (i32, [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_ExpertsMx), vp, ctypes.c_float,
+                                    vp, vp, vp, sz, vp]),
+        "moe_bias_update": (i32, [vp, ctypes.c_int32, ctypes.c_float, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -386,6 +392,73 @@ def forward(x, weights: Dict, K: int, routed_scaling: float = 5.0, *, out=None, 
     _check(lib.moe_forward(ctypes.byref(d), ctypes.byref(wstruct), _ptr(x), _ptr(out), _ptr(w),
                            w.numel() * w.element_size(), _stream(stream)))
     return out
+
+
+# ----------------------------------------------------------------------------
+# the layer's neighbours: pre-norm, residual (the block), bias update
+# ----------------------------------------------------------------------------
+
+RMS_EPS = 1e-5
+
+
+def rmsnorm(x, gamma, eps: float = RMS_EPS, *, out=None, stream=None):
+    """moe_rmsnorm: y = bf16(gamma * bf16(x * rsqrt(mean(x^2) + eps))) per row; x [T, H], gamma [H] bf16."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise TypeError("x must be a [T, H] torch tensor")
+    T, H = x.shape
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, H), dev)
+    _need(gamma, "gamma", torch.bfloat16, (H,), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    _check(load_library().moe_rmsnorm(_ptr(x), _ptr(gamma), T, H, eps, _ptr(out), _stream(stream)))
+    return out
+
+
+def block_workspace_bytes(dims: MoEDims) -> int:
+    return int(load_library().moe_block_workspace_bytes(ctypes.byref(dims.c())))
+
+
+def block_forward(x, weights: Dict, gamma, K: int, routed_scaling: float = 5.0, eps: float = RMS_EPS, *, mx=None,
+                  out=None, ws=None, stream=None, n_group: int = 1, topk_group: int = 1):
+    """moe_block_forward: out = x + LatentMoE(RMSNorm(x)); ``mx`` optional MXFP8 experts (T <= 64).
+    ``out`` may be ``x`` (in place)."""
+    torch = _torch()
+    if mx is None:
+        dims = dims_from(x, weights, K, routed_scaling, n_group, topk_group)
+    else:
+        dims = dims_from_mx(x, weights, mx, K, routed_scaling, n_group, topk_group)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (dims.T, dims.H), dev)
+    _need(gamma, "gamma", torch.bfloat16, (dims.H,), dev)
+    wstruct = _weight_struct(dims, weights, dev, experts=mx is None)
+    mstruct = None if mx is None else ctypes.byref(_mx_struct(dims, mx, dev))
+    d = dims.c()
+    lib = load_library()
+    if out is None:
+        out = torch.empty(dims.T, dims.H, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (dims.T, dims.H), dev)
+    nbytes = lib.moe_block_workspace_bytes(ctypes.byref(d))
+    if nbytes == 0:
+        _check(lib.moe_block_forward(ctypes.byref(d), ctypes.byref(wstruct), mstruct, None, eps, None, None, None, 0,
+                                     None))
+    w = _workspace(nbytes, dev, ws)
+    _check(lib.moe_block_forward(ctypes.byref(d), ctypes.byref(wstruct), mstruct, _ptr(gamma), eps, _ptr(x),
+                                 _ptr(out), _ptr(w), w.numel() * w.element_size(), _stream(stream)))
+    return out
+
+
+def bias_update(offsets, corr_bias, eta: float, *, stream=None):
+    """moe_bias_update: corr_bias[i] -= eta * (load_i - mean load), load from the expert offsets [E+1]."""
+    torch = _torch()
+    E = corr_bias.shape[0]
+    dev = corr_bias.device
+    _need(corr_bias, "corr_bias", torch.float32, (E,), dev)
+    _need(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _check(load_library().moe_bias_update(_ptr(offsets), E, eta, _ptr(corr_bias), _stream(stream)))
+    return corr_bias
 
 
 class PhaseEvents:

@@ -58,6 +58,8 @@ struct GemmProblem {
   void* C;
   int64_t ldc;
   int epi;
+  const uint16_t* residual;  // nullable, dense bf16 epilogues: C = bf16(residual + bf16(acc))
+  int64_t ldr;
   int mtiles;                // M tiles in the grid (an upper bound in grouped mode)
   int ntiles;                // ceil(N / BN)
   int group_m;               // M tiles per raster group
@@ -425,8 +427,24 @@ gemm_bf16_kernel(const GemmLaunch L) {
       const int n = n0 + wave_n * WTN + c * 8;
       if (m >= mend || n >= P.N) continue;
       uint16_t* dst = static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n;
-      if (n + 8 <= P.N) *reinterpret_cast<u32x4*>(dst) = v;
-      else *reinterpret_cast<u32x2*>(dst) = u32x2{v[0], v[1]};   // N is a multiple of 4
+      const bool full = n + 8 <= P.N;                 // else 4 columns (N is a multiple of 4)
+      u32x4 o = v;
+      if (EPI < 0 && P.residual != nullptr) {
+        // the block's residual add: bf16 + bf16 in fp32 (exact), rounded once
+        const uint16_t* src = P.residual + (int64_t)m * P.ldr + n;
+        u32x4 rv;
+        if (full) rv = *reinterpret_cast<const u32x4*>(src);
+        else {
+          const u32x2 h = *reinterpret_cast<const u32x2*>(src);
+          rv = u32x4{h[0], h[1], 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = cvt_pk_bf16(bf16_bits_to_f32(v[q] & 0xFFFFu) + bf16_bits_to_f32(rv[q] & 0xFFFFu),
+                             bf16_bits_to_f32(v[q] >> 16) + bf16_bits_to_f32(rv[q] >> 16));
+      }
+      if (full) *reinterpret_cast<u32x4*>(dst) = o;
+      else *reinterpret_cast<u32x2*>(dst) = u32x2{o[0], o[1]};
     }
   };
   if constexpr (kHalfTiles) {

@@ -43,6 +43,9 @@ struct SkinnyProblem {
   // and E8M0 scales, one per 32 k; seg[0].B is then unused
   const uint8_t* mx_codes;
   const uint8_t* mx_scales;
+  // nullable, dense bf16 epilogue: C = bf16(residual + bf16(acc)) (the block's residual add)
+  const uint16_t* residual;
+  int64_t ldr;
 };
 hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st);
 hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t nblocks, uint8_t* codes, uint8_t* scales,
@@ -68,6 +71,9 @@ hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, 
                                int32_t* offsets, int32_t* row_token, int32_t* slot_row, hipStream_t st);
 hipError_t launch_gather_rows(const uint16_t* src, int C, const int32_t* row_token, int64_t rows, uint16_t* dst,
                               hipStream_t st);
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, int64_t T, int H, float eps, uint16_t* y,
+                          hipStream_t st);
+hipError_t launch_bias_update(const int32_t* offsets, int E, float eta, float* bias, hipStream_t st);
 hipError_t launch_combine(const uint16_t* y, const float* gate, const int32_t* slot_row, int T, int K, int L,
                           uint16_t* y_lat, hipStream_t st);
 

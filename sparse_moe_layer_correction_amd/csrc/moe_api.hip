@@ -264,7 +264,7 @@ PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 101; }
+int moe_abi_version(void) { return 102; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -355,10 +355,28 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* s
 namespace {
 
 // mx: MXFP8 expert weights (then w->w_up / w->w_down are not read), or null.
+// The block around the layer: x_in is normed into the workspace (after the
+// layer's own scratch) and is the residual of the output.
+struct BlockArgs {
+  const uint16_t* x_in;
+  const uint16_t* gamma;
+  float eps;
+};
+
+size_t block_extra_bytes(const moe_dims& d) { return align_up((size_t)d.T * d.H * 2); }
+
+bool eps_ok(float eps) { return eps >= 0.f && eps <= 1e30f; }   // also rejects NaN
+
 int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
-                 size_t ws_bytes, hipStream_t stream, const Marks& mk, const moe_experts_mx* mx = nullptr) {
+                 size_t ws_bytes, hipStream_t stream, const Marks& mk, const moe_experts_mx* mx = nullptr,
+                 const BlockArgs* blk = nullptr) {
   int st;
   if (!dims_ok(dims, &st)) return st;
+  if (blk != nullptr) {
+    if (!blk->x_in || !blk->gamma || !eps_ok(blk->eps)) return MOE_ERR_INVALID;
+    if (((uintptr_t)blk->x_in | (uintptr_t)blk->gamma) & 15) return MOE_ERR_INVALID;
+    x = blk->x_in;                                  // checked below; replaced by the normed rows
+  }
   if (!w || !x || !out || !w->w_router || !w->corr_bias || !w->w_fc1 || !w->w_fc2 || !w->w_sh_up || !w->w_sh_down)
     return MOE_ERR_INVALID;
   if (mx != nullptr) {
@@ -370,7 +388,15 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   }
   const moe_dims& d = *dims;
   const Layout l = make_layout(d);
-  if (!ws_ok(ws, ws_bytes, l.total)) return MOE_ERR_WORKSPACE;
+  if (!ws_ok(ws, ws_bytes, l.total + (blk ? block_extra_bytes(d) : 0))) return MOE_ERR_WORKSPACE;
+  const uint16_t* residual = nullptr;
+  if (blk != nullptr) {
+    // 0. the pre-norm: x = RMSNorm(x_in) into the workspace; x_in is the residual
+    uint16_t* xn = at<uint16_t>(ws, l.total);
+    if (launch_rmsnorm(blk->x_in, blk->gamma, d.T, d.H, blk->eps, xn, stream) != hipSuccess) return MOE_ERR_HIP;
+    x = xn;
+    residual = blk->x_in;
+  }
   const int64_t T = d.T, H = d.H, L = d.L, I = d.I, Is = d.Is, TK = T * d.K;
 
   int32_t* idx = at<int32_t>(ws, l.idx);
@@ -489,6 +515,8 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   if (skinny) {
     if (mk.mark(MOE_PHASE_FC2_SHARED_DOWN) != hipSuccess) return MOE_ERR_HIP;
     SkinnyProblem P = skinny_dense(d.T, d.H, d.H, out, H, EPI_BF16, d.L + d.Is, partial);
+    P.residual = residual;
+    P.ldr = H;
     add_seg(P, y_lat, L, w->w_fc2, L, d.L);
     add_seg(P, hs, Is, w->w_sh_down, Is, d.Is);
     if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
@@ -497,6 +525,8 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     GemmLaunch G{};
     G.np = 1;
     G.p[0] = dense_problem(cfg, d.T, d.H, d.H, out, H, EPI_BF16);
+    G.p[0].residual = residual;
+    G.p[0].ldr = H;
     add_seg(G.p[0], y_lat, L, w->w_fc2, L, d.L);
     add_seg(G.p[0], hs, Is, w->w_sh_down, Is, d.Is);
     if (mk.mark(MOE_PHASE_FC2_SHARED_DOWN) != hipSuccess) return MOE_ERR_HIP;
@@ -537,6 +567,32 @@ int moe_forward_mx_profiled(const moe_dims* dims, const moe_weights* w, const mo
   for (int i = 0; i < MOE_N_PHASES + 1; ++i)
     if (events[i] == nullptr) return MOE_ERR_INVALID;
   return forward_impl(dims, w, x, out, ws, ws_bytes, stream, Marks{events, stream}, mx);
+}
+
+int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, int64_t T, int32_t H, float eps, uint16_t* y,
+                hipStream_t stream) {
+  if (x == nullptr || gamma == nullptr || y == nullptr || T <= 0 || H <= 0 || H % 8 || !eps_ok(eps))
+    return MOE_ERR_INVALID;
+  if (((uintptr_t)x | (uintptr_t)gamma | (uintptr_t)y) & 15) return MOE_ERR_INVALID;
+  return hip_status(launch_rmsnorm(x, gamma, T, H, eps, y, stream));
+}
+
+size_t moe_block_workspace_bytes(const moe_dims* dims) {
+  int st;
+  if (!dims_ok(dims, &st)) return 0;
+  return make_layout(*dims).total + block_extra_bytes(*dims);
+}
+
+int moe_block_forward(const moe_dims* dims, const moe_weights* w, const moe_experts_mx* mx, const uint16_t* gamma,
+                      float eps, const uint16_t* x, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const BlockArgs blk{x, gamma, eps};
+  return forward_impl(dims, w, nullptr, out, ws, ws_bytes, stream, Marks{nullptr, stream}, mx, &blk);
+}
+
+int moe_bias_update(const int32_t* offsets, int32_t E, float eta, float* corr_bias, hipStream_t stream) {
+  if (offsets == nullptr || corr_bias == nullptr || E <= 0 || !(eta == eta) || eta > 1e30f || eta < -1e30f)
+    return MOE_ERR_INVALID;
+  return hip_status(launch_bias_update(offsets, E, eta, corr_bias, stream));
 }
 
 int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,

@@ -49,6 +49,17 @@ __device__ __forceinline__ u32x4 mx_decode8(u32x2 c, uint32_t s) {
 #define MOE_GROUPED_WIDE_WAVES (1 << 30)
 #endif
 
+// Four results rounded to bf16, each added to its bf16 residual in fp32 (exact)
+// and rounded once more: the block's residual add.
+__device__ __forceinline__ u32x2 add_residual_bf16x4(const f32x4v& v, const uint16_t* res) {
+  const u32x2 r = *reinterpret_cast<const u32x2*>(res);
+  float o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = bf16_bits_to_f32(f32_to_bf16_bits(v[i])) + bf16_bits_to_f32((r[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
+  return u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+}
+
 int skinny_slabs_per_wave(const SkinnyProblem& P) {
   if (P.offsets == nullptr) return P.M > 16 ? 4 : 1;
   return (int64_t)P.groups * ((P.N + 63) / 64) >= MOE_GROUPED_WIDE_WAVES ? 4 : 1;
@@ -192,7 +203,8 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
           v[0] = relu2(v[0]); v[1] = relu2(v[1]); v[2] = relu2(v[2]); v[3] = relu2(v[3]);
         }
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)(out_row0 + m) * P.ldc + n) =
-            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            P.residual ? add_residual_bf16x4(v, P.residual + (int64_t)(out_row0 + m) * P.ldr + n)
+                       : u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
     }
   }
@@ -257,7 +269,8 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
 
 // out[m, n] = epi(sum_{s < ksplit} partial[s, m, n]), summed in split order.
 __global__ void __launch_bounds__(256) skinny_reduce_kernel(const float* __restrict__ partial, int ksplit, int M, int N,
-                                                            void* C, int64_t ldc, int epi) {
+                                                            void* C, int64_t ldc, int epi,
+                                                            const uint16_t* __restrict__ residual, int64_t ldr) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   const int64_t total = (int64_t)M * N;
   if (i >= total) return;
@@ -271,7 +284,8 @@ __global__ void __launch_bounds__(256) skinny_reduce_kernel(const float* __restr
       s[0] = relu2(s[0]); s[1] = relu2(s[1]); s[2] = relu2(s[2]); s[3] = relu2(s[3]);
     }
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) =
-        u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+        residual ? add_residual_bf16x4(s, residual + (int64_t)m * ldr + n)
+                 : u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
   }
 }
 
@@ -306,7 +320,7 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
   if (e != hipSuccess || P.partial == nullptr) return e;
   const int64_t total = (int64_t)P.M * P.N;
   hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, st, P.partial,
-                     P.ksplit, P.M, P.N, P.C, P.ldc, P.epi);
+                     P.ksplit, P.M, P.N, P.C, P.ldc, P.epi, P.residual, P.ldr);
   return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 101
+    assert lib.moe_abi_version() == 102
 
 
 def test_status_strings(lib):
@@ -173,3 +173,32 @@ def test_mxfp8_entry_points_validate_before_any_launch(lib):
     assert lib.moe_forward(d, ctypes.byref(w), 256, 256, 256, need, None) == -1
     ev = (ctypes.c_void_p * 8)()
     assert lib.moe_forward_mx_profiled(d, ctypes.byref(w), ctypes.byref(mx), 256, 256, 256, need, None, ev, 8) == -1
+
+
+def test_block_entry_points_validate_before_any_launch(lib):
+    d = _d(TINY)
+    need = lib.moe_workspace_bytes(d)
+    bneed = lib.moe_block_workspace_bytes(d)
+    assert bneed == need + TINY.T * TINY.H * 2           # the normed rows (256-byte multiple here)
+    w = M._Weights(*([256] * 8))
+    f = lib.moe_block_forward
+    assert f(d, ctypes.byref(w), None, None, 1e-5, 256, 256, 256, bneed, None) == -1    # no gamma
+    assert f(d, ctypes.byref(w), None, 264, 1e-5, 256, 256, 256, bneed, None) == -1     # misaligned gamma
+    assert f(d, ctypes.byref(w), None, 256, -1.0, 256, 256, 256, bneed, None) == -1     # bad eps
+    assert f(d, ctypes.byref(w), None, 256, float("nan"), 256, 256, 256, bneed, None) == -1
+    assert f(d, ctypes.byref(w), None, 256, 1e-5, None, 256, 256, bneed, None) == -1    # no x
+    assert f(d, ctypes.byref(w), None, 256, 1e-5, 256, 256, 256, bneed - 1, None) == -3  # workspace
+    assert f(d, ctypes.byref(w), None, 256, 1e-5, 256, 256, 256, need, None) == -3
+    bad = M.MoEDims(TINY.T, 100, TINY.L, TINY.E, TINY.I, TINY.K, TINY.Is)
+    assert lib.moe_block_workspace_bytes(_d(bad)) == 0
+    n = lib.moe_rmsnorm
+    assert n(256, 256, 4, 60, 1e-5, 256, None) == -1      # H not a multiple of 8
+    assert n(256, 256, 0, 64, 1e-5, 256, None) == -1
+    assert n(None, 256, 4, 64, 1e-5, 256, None) == -1
+    assert n(256, 256, 4, 64, 1e-5, 264, None) == -1      # misaligned output
+    assert n(256, 256, 4, 64, float("inf"), 256, None) == -1
+    b = lib.moe_bias_update
+    assert b(None, 8, 1e-3, 256, None) == -1
+    assert b(256, 0, 1e-3, 256, None) == -1
+    assert b(256, 8, float("nan"), 256, None) == -1
+    assert b(256, 8, 1e-3, None, None) == -1
