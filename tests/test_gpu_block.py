@@ -45,7 +45,9 @@ def _dev(bits: np.ndarray):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,H,scale,eps", [(64, 256, 1.0, EPS), (37, 8192, 3.0, EPS), (1, 8192, 1.0, EPS),
-                                           (300, 2048, 1e-3, EPS), (5, 64, 40.0, 0.0), (16, 8, 1.0, 0.5)])
+                                           (300, 2048, 1e-3, EPS), (5, 64, 40.0, 0.0), (16, 8, 1.0, 0.5),
+                                           # 2, 6 and more than 8 16-byte chunks per thread
+                                           (3, 4096, 1.0, EPS), (4, 12288, 2.0, EPS), (3, 20480, 1.0, EPS)])
 def test_rmsnorm_bit_exact(T, H, scale, eps):
     g = torch.Generator().manual_seed(T * 1000 + H)
     x = (scale * torch.randn(T, H, generator=g)).to(torch.bfloat16)
