@@ -228,6 +228,9 @@ def main():
 
     offsets = ws[lay["offsets"]:lay["offsets"] + 4 * (cfg.E + 1)].view(torch.int32).cpu().numpy()
     n_touched = int(np.count_nonzero(np.diff(offsets)))
+    loads = np.diff(offsets)
+    gap = ws[lay["gap"]:lay["gap"] + 4 * cfg.T].view(torch.float32).cpu().numpy()
+    near_ties = int(np.count_nonzero(gap < 1e-4))
     # rows the grouped 256-row tiles cover (each expert's tail tile is padded)
     m_tiles = int(np.sum((np.diff(offsets) + 255) // 256))
     idx_gpu = ws[lay["idx"]:lay["idx"] + 4 * cfg.T * cfg.K].view(torch.int32).view(cfg.T, cfg.K).cpu().numpy()
@@ -284,6 +287,8 @@ def main():
         "hbm_gbs_layer": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "hbm_frac_layer": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "experts_touched": n_touched,
+        "load_max_over_mean": round(float(loads.max() / loads.mean()), 3),
+        "near_tie_tokens": near_ties,
         "grouped_m_tiles": m_tiles,
         "grouped_row_padding": round(1 - cfg.T * cfg.K / max(1, m_tiles * 256), 4),
         "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
