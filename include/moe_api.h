@@ -71,7 +71,9 @@ typedef struct moe_dims {
  *   w_down    [E, L, I] bf16   expert down projections
  *   w_fc2     [H, L]    bf16   fc2_latent_proj
  *   w_sh_up   [Is, H]   bf16   shared expert up
- *   w_sh_down [H, Is]   bf16   shared expert down */
+ *   w_sh_down [H, Is]   bf16   shared expert down
+ * Every weight and activation pointer must be 16-byte aligned (the kernels
+ * move 16 bytes per lane); moe_forward rejects others with MOE_ERR_INVALID. */
 typedef struct moe_weights {
   const float* w_router;
   const float* corr_bias;
@@ -117,8 +119,9 @@ typedef struct moe_ws_layout {
  *   ws        device workspace of at least moe_route_workspace_bytes(dims) bytes,
  *             256-byte aligned
  * The logits are accumulated in fp32 from exact bf16 x fp32 products (the fp32
- * weight is split into three bf16 parts); only the summation order differs
- * from an exact fp32 dot product. */
+ * weight is split exactly into three bf16 parts: by a pass over the weight for
+ * the tiled product, in registers for forwards of at most 64 tokens); only the
+ * summation order differs from an exact fp32 dot product. */
 size_t moe_route_workspace_bytes(const moe_dims* dims);
 int moe_route(const moe_dims* dims, const uint16_t* x, const float* w_router,
               const float* corr_bias, int32_t* topk_idx, float* topk_gate, float* topk_gap,

@@ -56,13 +56,29 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// max(v, the value DPP control CTRL brings from another lane), 0 (the identity
+// of an unsigned max) where the control brings nothing
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, ROW_MASK, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, true);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Max over the 64 lanes, returned to every lane. DPP moves (VALU latency) rather
+// than LDS permutes: row shifts by 1, 2, 4, 8 leave each 16-lane row's max in
+// its lane 15; broadcasts of lane 15 and lane 31 carry it to the last lane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_u64<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_max_u64<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_max_u64<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_max_u64<0x118, 0xF>(v);   // row_shr:8
+  v = dpp_max_u64<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max_u64<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {

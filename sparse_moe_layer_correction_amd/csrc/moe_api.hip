@@ -227,14 +227,20 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
               float* partial = nullptr) {
   uint16_t* parts = at<uint16_t>(ws, l.wsplit);
   float* logits = at<float>(ws, l.logits);
+  const bool skinny = d.T <= kSkinnyMaxT && partial != nullptr;
+  hipError_t e = hipSuccess;
   if (mk.mark(MOE_PHASE_ROUTER_SPLIT) != hipSuccess) return MOE_ERR_HIP;
-  hipError_t e = launch_split_router_weight(w_router, d.E, d.H, parts, st);
+  // the tiled GEMM reads the fp32 weight as three bf16 parts written here; the
+  // few-token product splits it in registers instead (no pass, 16 instead of
+  // 24 + 16 bytes of traffic per weight)
+  if (!skinny) e = launch_split_router_weight(w_router, d.E, d.H, parts, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int64_t EH = (int64_t)d.E * d.H;
   if (mk.mark(MOE_PHASE_ROUTER_GEMM) != hipSuccess) return MOE_ERR_HIP;
-  if (d.T <= kSkinnyMaxT && partial != nullptr) {
-    SkinnyProblem P = skinny_dense(d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32, 3 * d.H, partial);
-    for (int s = 0; s < 3; ++s) add_seg(P, x, d.H, parts + s * EH, d.H, d.H);
+  if (skinny) {
+    SkinnyProblem P = skinny_dense(d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32, d.H, partial);
+    add_seg(P, x, d.H, nullptr, d.H, d.H);
+    P.f32_b = w_router;
     e = launch_skinny(P, st);
   } else {
     const int cfg = choose_dense_cfg(d.T, (int)l.ldl);
@@ -379,6 +385,13 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   }
   if (!w || !x || !out || !w->w_router || !w->corr_bias || !w->w_fc1 || !w->w_fc2 || !w->w_sh_up || !w->w_sh_down)
     return MOE_ERR_INVALID;
+  {
+    // 16-byte loads and stores per lane
+    uintptr_t a = (uintptr_t)x | (uintptr_t)out | (uintptr_t)w->w_router | (uintptr_t)w->w_fc1 |
+                  (uintptr_t)w->w_fc2 | (uintptr_t)w->w_sh_up | (uintptr_t)w->w_sh_down;
+    if (mx == nullptr) a |= (uintptr_t)w->w_up | (uintptr_t)w->w_down;
+    if (a & 15) return MOE_ERR_INVALID;
+  }
   if (mx != nullptr) {
     if (!mx->w_up || !mx->w_up_scale || !mx->w_down || !mx->w_down_scale) return MOE_ERR_INVALID;
     if (((uintptr_t)mx->w_up | (uintptr_t)mx->w_down) & 15) return MOE_ERR_INVALID;

@@ -60,6 +60,29 @@ __device__ __forceinline__ u32x2 add_residual_bf16x4(const f32x4v& v, const uint
   return u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
 }
 
+// 8 fp32 weights (a: k 0..3, b: k 4..7) split exactly into three bf16x8 MFMA
+// operands: hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (each
+// difference is exact, and the three parts sum to w).
+__device__ __forceinline__ void split3_bf16x8(const u32x4 a, const u32x4 b, u32x4 (&part)[3]) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = __uint_as_float(a[i]);
+    r[4 + i] = __uint_as_float(b[i]);
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    uint32_t bits[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bits[i] = f32_to_bf16_bits(r[i]);
+      r[i] -= bf16_bits_to_f32(bits[i]);
+    }
+    part[q] = u32x4{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16), bits[4] | (bits[5] << 16),
+                    bits[6] | (bits[7] << 16)};
+  }
+}
+
 int skinny_slabs_per_wave(const SkinnyProblem& P) {
   if (P.offsets == nullptr) return P.M > 16 ? 4 : 1;
   return (int64_t)P.groups * ((P.N + 63) / 64) >= MOE_GROUPED_WIDE_WAVES ? 4 : 1;
@@ -70,10 +93,13 @@ int skinny_slabs_per_wave(const SkinnyProblem& P) {
 // holds k = 16g .. 16g+15 of the step (the first MFMA takes its low 8, the
 // second its high 8), so a lane's weights of a step are 16 consecutive
 // elements: two 16-byte loads of bf16, or one 16-byte load of MXFP8 codes plus
-// the one scale byte they share. The activations are loaded in the same k
-// order, so the products are unchanged; per step the wave issues MT*NS*2
-// MFMAs and reads the activations once per NS weight fragments.
-template <int MT, int NS, int UNROLL, bool MX>
+// the one scale byte they share, or four 16-byte loads of fp32 weights (the
+// router's), each split exactly into three bf16 parts hi + mid + lo that take
+// one MFMA each. The activations are loaded in the same k order, so the
+// products are unchanged; per step the wave issues MT*NS*2 MFMAs (three times
+// that for fp32 weights) and reads the activations once per NS weight
+// fragments.
+template <int MT, int NS, int UNROLL, int BMODE>
 __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first, int rows, int row0,
                                             const int32_t* gather, int64_t b_base, int k_begin, int k_end,
                                             int out_row0, float* partial, int lane, int epi) {
@@ -94,10 +120,11 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[j][t] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-  // what one lane loads for one slab in one step: bf16 weights (two fragments)
-  // or MXFP8 codes (decoded at use) and their block scale
+  constexpr bool MX = BMODE == kSkinnyMx, F32 = BMODE == kSkinnyF32;
+  // what one lane loads for one slab in one step: bf16 weights (w[0..1]), MXFP8
+  // codes (w[0], decoded at use) and their block scale, or fp32 weights (w[0..3])
   struct BRaw {
-    u32x4 w0, w1;
+    u32x4 w[4];
     uint32_t s;
   };
 
@@ -110,23 +137,30 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
       const uint16_t* bp[NS];
       const uint8_t* cp[NS];                 // MX: codes and the block scale of this lane's k
       const uint8_t* sp[NS];
+      const float* fp[NS];                   // fp32 weights
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
+        const int64_t e0 = b_base + (int64_t)nrow[j] * S.ldb + (lo - seg_k0) + kl;
         if constexpr (MX) {
-          cp[j] = P.mx_codes + b_base + (int64_t)nrow[j] * S.ldb + (lo - seg_k0) + kl;
+          cp[j] = P.mx_codes + e0;
           sp[j] = P.mx_scales + b_base / 32 + (int64_t)nrow[j] * (S.ldb / 32) + (lo - seg_k0 + kl) / 32;
+        } else if constexpr (F32) {
+          fp[j] = P.f32_b + e0;
         } else {
-          bp[j] = S.B + b_base + (int64_t)nrow[j] * S.ldb + (lo - seg_k0) + kl;
+          bp[j] = S.B + e0;
         }
       }
       auto load_b = [&](int j, int st) -> BRaw {
         BRaw r;
         if constexpr (MX) {
-          r.w0 = *reinterpret_cast<const u32x4*>(cp[j] + st * 64);
+          r.w[0] = *reinterpret_cast<const u32x4*>(cp[j] + st * 64);
           r.s = sp[j][st * 2];
+        } else if constexpr (F32) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) r.w[q] = *reinterpret_cast<const u32x4*>(fp[j] + st * 64 + 4 * q);
         } else {
-          r.w0 = *reinterpret_cast<const u32x4*>(bp[j] + st * 64);
-          r.w1 = *reinterpret_cast<const u32x4*>(bp[j] + st * 64 + 8);
+          r.w[0] = *reinterpret_cast<const u32x4*>(bp[j] + st * 64);
+          r.w[1] = *reinterpret_cast<const u32x4*>(bp[j] + st * 64 + 8);
         }
         return r;
       };
@@ -136,17 +170,34 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
       auto mfma_step = [&](const BRaw (&b)[NS], const u32x4 (&a0)[MT], const u32x4 (&a1)[MT]) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          u32x4 w0 = b[j].w0, w1 = b[j].w1;
-          if constexpr (MX) {
-            w1 = mx_decode8(u32x2{b[j].w0.z, b[j].w0.w}, b[j].s);
-            w0 = mx_decode8(u32x2{b[j].w0.x, b[j].w0.y}, b[j].s);
-          }
+          if constexpr (F32) {
 #pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0),
-                                                                __builtin_bit_cast(bf16x8, a0[t]), acc[j][t], 0, 0, 0);
-            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1),
-                                                                __builtin_bit_cast(bf16x8, a1[t]), acc[j][t], 0, 0, 0);
+            for (int h = 0; h < 2; ++h) {
+              u32x4 part[3];
+              split3_bf16x8(b[j].w[2 * h], b[j].w[2 * h + 1], part);
+#pragma unroll
+              for (int q = 0; q < 3; ++q)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                  acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      __builtin_bit_cast(bf16x8, part[q]), __builtin_bit_cast(bf16x8, h ? a1[t] : a0[t]), acc[j][t],
+                      0, 0, 0);
+            }
+          } else {
+            u32x4 w0 = b[j].w[0], w1 = b[j].w[1];
+            if constexpr (MX) {
+              w1 = mx_decode8(u32x2{b[j].w[0].z, b[j].w[0].w}, b[j].s);
+              w0 = mx_decode8(u32x2{b[j].w[0].x, b[j].w[0].y}, b[j].s);
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+              acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0),
+                                                                  __builtin_bit_cast(bf16x8, a0[t]), acc[j][t], 0, 0,
+                                                                  0);
+              acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1),
+                                                                  __builtin_bit_cast(bf16x8, a1[t]), acc[j][t], 0, 0,
+                                                                  0);
+            }
           }
         }
       };
@@ -215,12 +266,12 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
 // GROUPED_EPI: -1 for dense products (epilogue from the problem), else the
 // fixed epilogue of a grouped expert product (which also names up and down
 // apart in profiles).
-constexpr int unroll_steps(int mt, int nsb, bool mx) {
-  const int u = MOE_SKINNY_INFLIGHT / (nsb * mt * (mx ? 16 : 32));
+constexpr int unroll_steps(int mt, int nsb, int bmode) {
+  const int u = MOE_SKINNY_INFLIGHT / (nsb * mt * (bmode == kSkinnyMx ? 16 : bmode == kSkinnyF32 ? 64 : 32));
   return u > 0 ? u : 1;
 }
 
-template <int NSB, int GROUPED_EPI, bool MX = false>
+template <int NSB, int GROUPED_EPI, int BMODE = kSkinnyBf16>
 __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -254,16 +305,16 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
   // up to 64 rows in registers per pass; more rows take further passes
   for (int r0 = 0; r0 < rows; r0 += 64) {
     const int rr = min(64, rows - r0);
-    // steps in flight per lane: about 128 bytes of weights (MXFP8 codes are half as large)
+    // steps in flight per lane: about 128 bytes of weights
     if (rr <= 16)
-      skinny_tile<1, NSB, unroll_steps(1, NSB, MX), MX>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
-                                                       row0 + r0, partial, lane, epi);
+      skinny_tile<1, NSB, unroll_steps(1, NSB, BMODE), BMODE>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin,
+                                                             k_end, row0 + r0, partial, lane, epi);
     else if (rr <= 32)
-      skinny_tile<2, NSB, unroll_steps(2, NSB, MX), MX>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
-                                                       row0 + r0, partial, lane, epi);
+      skinny_tile<2, NSB, unroll_steps(2, NSB, BMODE), BMODE>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin,
+                                                             k_end, row0 + r0, partial, lane, epi);
     else
-      skinny_tile<4, NSB, unroll_steps(4, NSB, MX), MX>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin, k_end,
-                                                       row0 + r0, partial, lane, epi);
+      skinny_tile<4, NSB, unroll_steps(4, NSB, BMODE), BMODE>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin,
+                                                             k_end, row0 + r0, partial, lane, epi);
   }
 }
 
@@ -289,6 +340,39 @@ __global__ void __launch_bounds__(256) skinny_reduce_kernel(const float* __restr
   }
 }
 
+// The same for few outputs and many splits (a decode router or fc1: hundreds of
+// outputs, tens of splits), where one thread per output would walk its splits
+// one dependent load after another: one wave per 4 outputs, lane l summing
+// splits l, l + 64, ..., then a fixed butterfly over the wave (the same order
+// every call).
+__global__ void __launch_bounds__(256) skinny_reduce_wide_kernel(const float* __restrict__ partial, int ksplit, int M,
+                                                                 int N, void* C, int64_t ldc, int epi,
+                                                                 const uint16_t* __restrict__ residual, int64_t ldr) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
+  const int64_t total = (int64_t)M * N;
+  if (i >= total) return;
+  f32x4v s = f32x4v{0.f, 0.f, 0.f, 0.f};
+  for (int k = lane; k < ksplit; k += 64) s += *reinterpret_cast<const f32x4v*>(partial + (int64_t)k * total + i);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] += __shfl_xor(s[q], m, 64);
+  }
+  if (lane != 0) return;
+  const int m = (int)(i / N), n = (int)(i % N);
+  if (epi == EPI_F32) {
+    *reinterpret_cast<f32x4v*>(static_cast<float*>(C) + (int64_t)m * ldc + n) = s;
+  } else {
+    if (epi == EPI_RELU2_BF16) {
+      s[0] = relu2(s[0]); s[1] = relu2(s[1]); s[2] = relu2(s[2]); s[3] = relu2(s[3]);
+    }
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) =
+        residual ? add_residual_bf16x4(s, residual + (int64_t)m * ldr + n)
+                 : u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+  }
+}
+
 hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
   // dense products carry up to 64 rows: 4 slabs per wave load the rows once per
   // four weight fragments; grouped products have a few rows per expert
@@ -299,16 +383,24 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
   const dim3 grid((unsigned)((tasks + 3) / 4)), block(256);
   if (P.offsets == nullptr) {
     if (P.mx_codes != nullptr) return hipErrorInvalidValue;     // MXFP8 weights: grouped products only
-    if (nsb == 4) hipLaunchKernelGGL((skinny_kernel<4, -1>), grid, block, 0, st, P);
-    else hipLaunchKernelGGL((skinny_kernel<1, -1>), grid, block, 0, st, P);
+    if (P.f32_b != nullptr) {                                   // fp32 weights: one K segment
+      if (P.nseg != 1) return hipErrorInvalidValue;
+      if (nsb == 4) hipLaunchKernelGGL((skinny_kernel<4, -1, kSkinnyF32>), grid, block, 0, st, P);
+      else hipLaunchKernelGGL((skinny_kernel<1, -1, kSkinnyF32>), grid, block, 0, st, P);
+    } else if (nsb == 4) {
+      hipLaunchKernelGGL((skinny_kernel<4, -1>), grid, block, 0, st, P);
+    } else {
+      hipLaunchKernelGGL((skinny_kernel<1, -1>), grid, block, 0, st, P);
+    }
   } else {
+    if (P.f32_b != nullptr) return hipErrorInvalidValue;        // fp32 weights: dense products only
     if (P.mx_codes != nullptr && P.nseg != 1) return hipErrorInvalidValue;
     const bool relu2 = P.epi == EPI_RELU2_BF16, mx = P.mx_codes != nullptr;
 #define MOE_GROUPED(NS)                                                                                       \
-  if (relu2 && mx) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16, true>), grid, block, 0, st, P);     \
-  else if (relu2) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16, false>), grid, block, 0, st, P);     \
-  else if (mx) hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16, true>), grid, block, 0, st, P);               \
-  else hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16, false>), grid, block, 0, st, P);
+  if (relu2 && mx) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16, kSkinnyMx>), grid, block, 0, st, P); \
+  else if (relu2) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16>), grid, block, 0, st, P);           \
+  else if (mx) hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16, kSkinnyMx>), grid, block, 0, st, P);         \
+  else hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16>), grid, block, 0, st, P);
     if (nsb == 4) {
       MOE_GROUPED(4)
     } else {
@@ -319,8 +411,12 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.partial == nullptr) return e;
   const int64_t total = (int64_t)P.M * P.N;
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, st, P.partial,
-                     P.ksplit, P.M, P.N, P.C, P.ldc, P.epi, P.residual, P.ldr);
+  if (P.ksplit >= 16 && total / 4 <= 4096)
+    hipLaunchKernelGGL(skinny_reduce_wide_kernel, dim3((unsigned)((total / 4 + 3) / 4)), dim3(256), 0, st, P.partial,
+                       P.ksplit, P.M, P.N, P.C, P.ldc, P.epi, P.residual, P.ldr);
+  else
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, st, P.partial,
+                       P.ksplit, P.M, P.N, P.C, P.ldc, P.epi, P.residual, P.ldr);
   return hipGetLastError();
 }
 

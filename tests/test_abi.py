@@ -132,6 +132,18 @@ def test_null_pointers_and_workspace_are_rejected_before_any_launch(lib):
     assert lib.moe_permute(d, 256, None, 0, None, 256, 256, 256, 256, pneed - 1, None) == -3
 
 
+def test_forward_rejects_misaligned_pointers(lib):
+    d = _d(TINY)
+    need = lib.moe_workspace_bytes(d)
+    ok = [256] * 8
+    for i in [0, 2, 3, 4, 5, 6, 7]:                      # every 16-byte-loaded weight (not the bias)
+        w = list(ok)
+        w[i] = 264
+        assert lib.moe_forward(d, ctypes.byref(M._Weights(*w)), 256, 256, 256, need, None) == -1, i
+    assert lib.moe_forward(d, ctypes.byref(M._Weights(*ok)), 258, 256, 256, need, None) == -1   # x
+    assert lib.moe_forward(d, ctypes.byref(M._Weights(*ok)), 256, 264, 256, need, None) == -1   # out
+
+
 def test_python_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
