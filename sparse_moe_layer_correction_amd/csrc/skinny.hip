@@ -43,11 +43,11 @@ __device__ __forceinline__ u32x4 mx_decode8(u32x2 c, uint32_t s) {
 #ifndef MOE_SKINNY_INFLIGHT
 #define MOE_SKINNY_INFLIGHT 128
 #endif
-// grouped products take 4 slabs per wave (activations reused 4x) when that
-// still leaves this many waves
-#ifndef MOE_GROUPED_WIDE_WAVES
-#define MOE_GROUPED_WIDE_WAVES (1 << 30)
-#endif
+// Grouped MXFP8 products with wide outputs take 4 slabs per wave (one set of
+// activation fragments serves 4 weight fragments) when that still leaves this
+// many waves: measured faster for the expert up product of a 64-token decode
+// (N = 5120), no better for N = 2048, and slower with bf16 weights.
+constexpr int64_t kGroupedWideWaves = 4096;
 
 // Four results rounded to bf16, each added to its bf16 residual in fp32 (exact)
 // and rounded once more: the block's residual add.
@@ -85,7 +85,8 @@ __device__ __forceinline__ void split3_bf16x8(const u32x4 a, const u32x4 b, u32x
 
 int skinny_slabs_per_wave(const SkinnyProblem& P) {
   if (P.offsets == nullptr) return P.M > 16 ? 4 : 1;
-  return (int64_t)P.groups * ((P.N + 63) / 64) >= MOE_GROUPED_WIDE_WAVES ? 4 : 1;
+  const bool wide = P.mx_codes != nullptr && P.N >= 4096 && (int64_t)P.groups * ((P.N + 63) / 64) >= kGroupedWideWaves;
+  return wide ? 4 : 1;
 }
 
 // MT m-tiles of 16 rows and NS slabs of 16 columns per wave. The k axis goes
@@ -302,6 +303,15 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
   const int n_first = blk * 16 * NSB;
   const int epi = GROUPED_EPI >= 0 ? GROUPED_EPI : P.epi;
 
+  if constexpr (BMODE == kSkinnyMx) {
+    // MXFP8 experts: passes of 16 rows (an expert of a decode batch has a few;
+    // more rows read its weights again). Keeping only the one-tile variant
+    // leaves room for twice the codes in flight per lane at the same occupancy.
+    for (int r0 = 0; r0 < rows; r0 += 16)
+      skinny_tile<1, NSB, unroll_steps(1, NSB, BMODE), BMODE>(P, n_first, min(16, rows - r0), row0 + r0, P.gather,
+                                                             b_base, k_begin, k_end, row0 + r0, partial, lane, epi);
+    return;
+  }
   // up to 64 rows in registers per pass; more rows take further passes
   for (int r0 = 0; r0 < rows; r0 += 64) {
     const int rr = min(64, rows - r0);
@@ -396,17 +406,18 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
     if (P.f32_b != nullptr) return hipErrorInvalidValue;        // fp32 weights: dense products only
     if (P.mx_codes != nullptr && P.nseg != 1) return hipErrorInvalidValue;
     const bool relu2 = P.epi == EPI_RELU2_BF16, mx = P.mx_codes != nullptr;
-#define MOE_GROUPED(NS)                                                                                       \
-  if (relu2 && mx) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16, kSkinnyMx>), grid, block, 0, st, P); \
-  else if (relu2) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16>), grid, block, 0, st, P);           \
-  else if (mx) hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16, kSkinnyMx>), grid, block, 0, st, P);         \
-  else hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16>), grid, block, 0, st, P);
-    if (nsb == 4) {
-      MOE_GROUPED(4)
+    if (nsb == 4) {                                             // MXFP8 only, see skinny_slabs_per_wave
+      if (relu2) hipLaunchKernelGGL((skinny_kernel<4, EPI_RELU2_BF16, kSkinnyMx>), grid, block, 0, st, P);
+      else hipLaunchKernelGGL((skinny_kernel<4, EPI_BF16, kSkinnyMx>), grid, block, 0, st, P);
+    } else if (relu2 && mx) {
+      hipLaunchKernelGGL((skinny_kernel<1, EPI_RELU2_BF16, kSkinnyMx>), grid, block, 0, st, P);
+    } else if (relu2) {
+      hipLaunchKernelGGL((skinny_kernel<1, EPI_RELU2_BF16>), grid, block, 0, st, P);
+    } else if (mx) {
+      hipLaunchKernelGGL((skinny_kernel<1, EPI_BF16, kSkinnyMx>), grid, block, 0, st, P);
     } else {
-      MOE_GROUPED(1)
+      hipLaunchKernelGGL((skinny_kernel<1, EPI_BF16>), grid, block, 0, st, P);
     }
-#undef MOE_GROUPED
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.partial == nullptr) return e;
