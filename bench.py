@@ -1,6 +1,6 @@
 """Benchmark of the LatentMoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ultra_prefill] [--experts bf16|mxfp8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ultra_prefill] [--experts bf16|mxfp8|mxfp4]
 
 A step is one whole forward (router, permutation, fc1 + shared up, expert up,
 expert down, combine, fc2 + shared down) over one batch of seeded synthetic
@@ -26,8 +26,8 @@ METRIC = "LatentMoE fwd tokens/s + TFLOP/s (Ultra shape); % MFMA peak / % HBM BW
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-# bytes per routed-expert weight element: bf16, or an E4M3 code plus 1/32 of an E8M0 scale
-EXPERT_WEIGHT_BYTES = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32}
+# bytes per routed-expert weight element: bf16, or an E4M3 / E2M1 code plus 1/32 of an E8M0 scale
+EXPERT_WEIGHT_BYTES = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32, "mxfp4": 0.5 + 1.0 / 32}
 
 
 def phase_work(cfg, n_touched: int, experts: str = "bf16"):
@@ -65,9 +65,12 @@ def cpu_baseline(d, cfg, idx_gpu, n_tokens: int, experts_fmt: str = "bf16"):
 
     def host_expert(e):
         up, down = u(d["w_up"][e]), u(d["w_down"][e])
-        if experts_fmt == "mxfp8":
+        if experts_fmt != "bf16":
+            q, dq = {"mxfp8": (oracle.quantize_mxfp8, oracle.dequantize_mxfp8),
+                     "mxfp4": (oracle.quantize_mxfp4, oracle.dequantize_mxfp4)}[experts_fmt]
+
             def deq(bits):
-                v = oracle.dequantize_mxfp8(*oracle.quantize_mxfp8(oracle.bf16_bits_to_f64(bits)))
+                v = dq(*q(oracle.bf16_bits_to_f64(bits)))
                 return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
             up, down = deq(up), deq(down)
         return up, down
@@ -87,7 +90,8 @@ def cpu_baseline(d, cfg, idx_gpu, n_tokens: int, experts_fmt: str = "bf16"):
     return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(tokens)} of the {cfg.T} tokens of the {cfg.name} batch (tokens are independent), "
                       f"whole layer per token in float64 with bf16 rounding"
-                      f"{' (MXFP8 experts, dequantised)' if experts_fmt == 'mxfp8' else ''}; {dt:.1f} s on "
+                      f"{f' ({experts_fmt.upper()} experts, dequantised)' if experts_fmt != 'bf16' else ''}; "
+                      f"{dt:.1f} s on "
                       f"{os.cpu_count()} host cores, BLAS threads {threads}"}
 
 
@@ -159,8 +163,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ultra_prefill",
                     choices=["ultra_prefill", "ultra_decode64", "ultra_decode1", "nano", "super", "tiny"])
-    ap.add_argument("--experts", default="bf16", choices=["bf16", "mxfp8"],
-                    help="routed experts' weights: bf16, or MXFP8 (few-token workloads, T <= 64)")
+    ap.add_argument("--experts", default="bf16", choices=["bf16", "mxfp8", "mxfp4"],
+                    help="routed experts' weights: bf16, or MXFP8 / MXFP4 (few-token workloads, T <= 64)")
     ap.add_argument("--block", action="store_true",
                     help="also time the block around the layer: RMSNorm + layer + residual, and the bias update")
     ap.add_argument("--cpu-tokens", type=int, default=8)
@@ -189,11 +193,11 @@ def main():
     out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
     lay = M.workspace_layout(dims)
     stream = torch.cuda.current_stream()
-    if args.experts == "mxfp8":
+    if args.experts != "bf16":
         if cfg.T > 64:
-            print("bench.py: MXFP8 experts are built for few-token forwards (T <= 64)", file=sys.stderr)
+            print("bench.py: MX experts are built for few-token forwards (T <= 64)", file=sys.stderr)
             sys.exit(2)
-        mx = M.quantize_experts_mxfp8(weights)
+        mx = M.quantize_experts_mx(weights, args.experts)
         run_w = {k: v for k, v in weights.items() if k not in ("w_up", "w_down")}
 
         def fwd():
@@ -302,7 +306,7 @@ def main():
         result["graph_ms_per_step"] = round(g_ms, 4)
         result["graph_tokens_per_s"] = round(cfg.T / (g_ms / 1e3), 1)
     if args.block:
-        result["block"] = block_timing(M, d, weights, cfg, args, mx if args.experts == "mxfp8" else None, ws, lay)
+        result["block"] = block_timing(M, d, weights, cfg, args, mx if args.experts != "bf16" else None, ws, lay)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, cfg, idx_gpu, args.cpu_tokens, args.experts)
     if args.calibrate_copy:

@@ -179,22 +179,26 @@ enum moe_phase {
 int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out,
                          void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events, int n_events);
 
-/* MXFP8 expert weights (OCP Microscaling format: FP8 E4M3 elements, one E8M0
- * power-of-two scale per 32 consecutive elements of a row). The released model
- * stores its experts block-scaled in 4 bits (the QA page on the experts' NVFP4
- * storage); this is the block-scaled format gfx950 decodes natively, at about
- * half the bytes of bf16, for the weight-bound few-token (decode) forward.
- *   w_up        device [E, I, L]    uint8 E4M3fn codes
+/* MX expert weights (OCP Microscaling formats: one E8M0 power-of-two scale per
+ * 32 consecutive elements of a row). The released model stores its experts
+ * block-scaled in 4 bits (the QA page on the experts' NVFP4 storage); these are
+ * the block-scaled formats gfx950 decodes natively, for the weight-bound
+ * few-token (decode) forward:
+ *   format 0 (MXFP8): FP8 E4M3fn elements, one byte each (about 1/2 of bf16);
+ *   format 1 (MXFP4): FP4 E2M1 elements, two per byte, element 2i in the low
+ *                     nibble of byte i (about 1/4 of bf16).
+ *   w_up        device [E, I, L]  or [E, I, L/2] (MXFP4) uint8 codes
  *   w_up_scale  device [E, I, L/32] uint8 E8M0 codes (scale 2^(code - 127))
- *   w_down      device [E, L, I]    uint8 E4M3fn codes
+ *   w_down      device [E, L, I]  or [E, L, I/2] (MXFP4) uint8 codes
  *   w_down_scale device [E, L, I/32] uint8 E8M0 codes
- * A weight's value is e4m3(code) * 2^(scale code - 127). The code tensors
+ * A weight's value is element(code) * 2^(scale code - 127). The code tensors
  * must be 16-byte aligned. */
 typedef struct moe_experts_mx {
   const uint8_t* w_up;
   const uint8_t* w_up_scale;
   const uint8_t* w_down;
   const uint8_t* w_down_scale;
+  int32_t format;          /* 0 = MXFP8 (E4M3), 1 = MXFP4 (E2M1) */
 } moe_experts_mx;
 
 /* Quantise bf16 weights src [rows, cols] (device, row-major; cols a multiple of
@@ -208,12 +212,23 @@ typedef struct moe_experts_mx {
 int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
                        hipStream_t stream);
 
-/* moe_forward with the routed experts' weights in MXFP8 (`mx`; w->w_up and
- * w->w_down are not read and may be NULL). Same workspace as moe_forward. The
+/* MXFP4 quantisation of bf16 weights src [rows, cols] (device, row-major; cols
+ * a multiple of 32) into packed codes [rows, cols/2] (element 2i in the low
+ * nibble of byte i) and scales [rows, cols/32] (device, caller owned). Per
+ * block of 32: e = floor(log2(max|v|)) - 2 clamped to [-127, 127] (an all-zero
+ * block: e = -127), scale code e + 127; each element is v * 2^-e rounded to the
+ * nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives), ties to the
+ * code with mantissa bit 0, saturating at 6. Errors as moe_quantize_mxfp8. */
+int moe_quantize_mxfp4(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream);
+
+/* moe_forward with the routed experts' weights in an MX format (`mx`; w->w_up
+ * and w->w_down are not read and may be NULL). Same workspace as moe_forward. The
  * expert products decode each weight to its exact bf16 value in registers and
  * run the bf16 path, so the results are those of moe_forward on the
  * dequantised weights. Few-token forwards only: T > 64 returns
- * MOE_ERR_UNSUPPORTED (the tiled expert products read bf16 weights). */
+ * MOE_ERR_UNSUPPORTED (the tiled expert products read bf16 weights); a format
+ * other than 0 or 1 returns MOE_ERR_INVALID. */
 int moe_forward_mx(const moe_dims* dims, const moe_weights* w, const moe_experts_mx* mx, const uint16_t* x,
                    uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 

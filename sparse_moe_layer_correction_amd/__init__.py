@@ -35,7 +35,7 @@ EXPORTS = (
     "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
     "moe_workspace_bytes", "moe_workspace_layout", "moe_forward", "moe_forward_profiled", "moe_status_string",
     "moe_abi_version", "moe_quantize_mxfp8", "moe_forward_mx", "moe_forward_mx_profiled",
-    "moe_rmsnorm", "moe_block_workspace_bytes", "moe_block_forward", "moe_bias_update",
+    "moe_rmsnorm", "moe_block_workspace_bytes", "moe_block_forward", "moe_bias_update", "moe_quantize_mxfp4",
 )
 
 # enum moe_phase of include/moe_api.h
@@ -59,7 +59,11 @@ class _Weights(ctypes.Structure):
 
 
 class _ExpertsMx(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w_up", "w_up_scale", "w_down", "w_down_scale")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_up", "w_up_scale", "w_down", "w_down_scale")] + \
+        [("format", ctypes.c_int32)]
+
+
+MX_FORMATS = {"mxfp8": 0, "mxfp4": 1}
 
 
 _LAYOUT_FIELDS = ("idx", "gate", "gap", "offsets", "row_token", "slot_row", "z", "h", "y", "y_lat", "hs", "total")
@@ -118,6 +122,7 @@ def load_library(path: Optional[str] = None):
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_abi_version": (i32, []),
         "moe_quantize_mxfp8": (i32, [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]),
+        "moe_quantize_mxfp4": (i32, [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]),
         "moe_forward_mx": (i32, [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_ExpertsMx), vp, vp, vp, sz, vp]),
         "moe_forward_mx_profiled": (i32, [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_ExpertsMx), vp, vp, vp,
                                           sz, vp, ctypes.POINTER(ctypes.c_void_p), i32]),
@@ -298,26 +303,51 @@ def quantize_mxfp8(w, *, stream=None):
     return codes, scales
 
 
+def quantize_mxfp4(w, *, stream=None):
+    """moe_quantize_mxfp4: bf16 [..., C] (C a multiple of 32) -> (packed codes uint8 [..., C/2],
+    scales uint8 [..., C/32])."""
+    torch = _torch()
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.bfloat16 or not w.is_cuda or not w.is_contiguous():
+        raise TypeError("w must be a contiguous bf16 CUDA tensor")
+    C = w.shape[-1]
+    rows = w.numel() // C
+    codes = torch.empty(w.shape[:-1] + (C // 2,), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(w.shape[:-1] + (C // 32,), dtype=torch.uint8, device=w.device)
+    _check(load_library().moe_quantize_mxfp4(_ptr(w), rows, C, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def quantize_experts_mx(weights: Dict, fmt: str = "mxfp8", *, stream=None) -> Dict:
+    """The routed experts' weights of ``weights`` in MX format ``fmt`` ("mxfp8" or "mxfp4"):
+    the keys of moe_experts_mx plus "format"."""
+    q = {"mxfp8": quantize_mxfp8, "mxfp4": quantize_mxfp4}[fmt]
+    up, up_s = q(weights["w_up"], stream=stream)
+    down, down_s = q(weights["w_down"], stream=stream)
+    return {"w_up": up, "w_up_scale": up_s, "w_down": down, "w_down_scale": down_s, "format": MX_FORMATS[fmt]}
+
+
 def quantize_experts_mxfp8(weights: Dict, *, stream=None) -> Dict:
     """The routed experts' weights of ``weights`` as MXFP8 (keys of moe_experts_mx)."""
-    up, up_s = quantize_mxfp8(weights["w_up"], stream=stream)
-    down, down_s = quantize_mxfp8(weights["w_down"], stream=stream)
-    return {"w_up": up, "w_up_scale": up_s, "w_down": down, "w_down_scale": down_s}
+    return quantize_experts_mx(weights, "mxfp8", stream=stream)
 
 
 def _mx_struct(dims: MoEDims, mx: Dict, dev):
     torch = _torch()
     E, L, I = dims.E, dims.L, dims.I
-    shapes = {"w_up": (E, I, L), "w_up_scale": (E, I, L // 32), "w_down": (E, L, I), "w_down_scale": (E, L, I // 32)}
+    fmt = int(mx.get("format", 0))
+    per = 2 if fmt == 1 else 1                      # elements per code byte
+    shapes = {"w_up": (E, I, L // per), "w_up_scale": (E, I, L // 32), "w_down": (E, L, I // per),
+              "w_down_scale": (E, L, I // 32)}
     for n, shp in shapes.items():
         _need(mx[n], n, torch.uint8, shp, dev)
-    return _ExpertsMx(*[_ptr(mx[n]) for n in ("w_up", "w_up_scale", "w_down", "w_down_scale")])
+    return _ExpertsMx(*[_ptr(mx[n]) for n in ("w_up", "w_up_scale", "w_down", "w_down_scale")], fmt)
 
 
 def dims_from_mx(x, weights: Dict, mx: Dict, K: int, routed_scaling: float = 5.0, n_group: int = 1,
                  topk_group: int = 1) -> MoEDims:
     T, H = x.shape
-    E, I, L = mx["w_up"].shape
+    E, I = mx["w_up"].shape[:2]
+    L = mx["w_up_scale"].shape[2] * 32
     Is = weights["w_sh_up"].shape[0]
     return MoEDims(T, H, L, E, I, K, Is, routed_scaling, n_group, topk_group)
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["router.hip", "permute.hip", "gemm.hip", "skinny.hip", "combine.hip", "mxfp8.hip", "norm.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "permute.hip", "gemm.hip", "skinny.hip", "combine.hip", "mx.hip", "norm.hip", "moe_api.hip"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 instructions
 COMMON_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -43,6 +43,7 @@ struct SkinnyProblem {
   // and E8M0 scales, one per 32 k; seg[0].B is then unused
   const uint8_t* mx_codes;
   const uint8_t* mx_scales;
+  int mx_fp4;                // MX codes are E2M1 (two per byte) rather than E4M3
   // fp32 weights (dense products, one K segment): when set, B is read from here
   // as fp32 [N, seg[0].ldb] and split exactly into three bf16 parts in registers
   const float* f32_b;
@@ -51,9 +52,11 @@ struct SkinnyProblem {
   int64_t ldr;
 };
 // the weight operand of a skinny product: bf16, MXFP8 codes and scales, or fp32
-enum SkinnyBMode : int { kSkinnyBf16 = 0, kSkinnyMx = 1, kSkinnyF32 = 2 };
+enum SkinnyBMode : int { kSkinnyBf16 = 0, kSkinnyMx = 1, kSkinnyF32 = 2, kSkinnyMx4 = 3 };
 hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st);
 hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t st);
+hipError_t launch_mxfp4_quantize(const uint16_t* src, int64_t nblocks, uint8_t* codes, uint8_t* scales,
                                  hipStream_t st);
 int skinny_slabs_per_wave(const SkinnyProblem& P);
 

@@ -270,7 +270,7 @@ PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 102; }
+int moe_abi_version(void) { return 103; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -394,6 +394,7 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   }
   if (mx != nullptr) {
     if (!mx->w_up || !mx->w_up_scale || !mx->w_down || !mx->w_down_scale) return MOE_ERR_INVALID;
+    if (mx->format != 0 && mx->format != 1) return MOE_ERR_INVALID;
     if (((uintptr_t)mx->w_up | (uintptr_t)mx->w_down) & 15) return MOE_ERR_INVALID;
     if (dims->T > kSkinnyMaxT) return MOE_ERR_UNSUPPORTED;   // the tiled expert products take bf16 only
   } else if (!w->w_up || !w->w_down) {
@@ -462,7 +463,7 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     SkinnyProblem P = skinny_grouped(std::min(d.E, d.T * d.K), ps, d.I, offsets, row_token, I * L, h, I,
                                      EPI_RELU2_BF16);
     add_seg(P, z, L, mx ? nullptr : w->w_up, L, d.L);
-    if (mx) { P.mx_codes = mx->w_up; P.mx_scales = mx->w_up_scale; }
+    if (mx) { P.mx_codes = mx->w_up; P.mx_scales = mx->w_up_scale; P.mx_fp4 = mx->format == 1; }
     if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
   } else {
     const TileShape ts = tile_shape(kGroupedCfg);
@@ -494,7 +495,7 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     if (mk.mark(MOE_PHASE_EXPERT_DOWN) != hipSuccess) return MOE_ERR_HIP;
     SkinnyProblem P = skinny_grouped(std::min(d.E, d.T * d.K), ps, d.L, offsets, nullptr, L * I, y, L, EPI_BF16);
     add_seg(P, h, I, mx ? nullptr : w->w_down, I, d.I);
-    if (mx) { P.mx_codes = mx->w_down; P.mx_scales = mx->w_down_scale; }
+    if (mx) { P.mx_codes = mx->w_down; P.mx_scales = mx->w_down_scale; P.mx_fp4 = mx->format == 1; }
     if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
   } else {
     const TileShape ts = tile_shape(kGroupedCfg);
@@ -580,6 +581,14 @@ int moe_forward_mx_profiled(const moe_dims* dims, const moe_weights* w, const mo
   for (int i = 0; i < MOE_N_PHASES + 1; ++i)
     if (events[i] == nullptr) return MOE_ERR_INVALID;
   return forward_impl(dims, w, x, out, ws, ws_bytes, stream, Marks{events, stream}, mx);
+}
+
+int moe_quantize_mxfp4(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream) {
+  if (rows <= 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID;
+  if (src == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID;
+  if (((uintptr_t)src | (uintptr_t)codes) & 15) return MOE_ERR_INVALID;
+  return hip_status(launch_mxfp4_quantize(src, rows * (cols / 32), codes, scales, stream));
 }
 
 int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, int64_t T, int32_t H, float eps, uint16_t* y,

@@ -43,7 +43,10 @@ __device__ __forceinline__ u32x4 mx_decode8(u32x2 c, uint32_t s) {
 #ifndef MOE_SKINNY_INFLIGHT
 #define MOE_SKINNY_INFLIGHT 128
 #endif
-// Grouped MXFP8 products with wide outputs take 4 slabs per wave (one set of
+#ifndef MOE_SKINNY_MX_INFLIGHT
+#define MOE_SKINNY_MX_INFLIGHT 256
+#endif
+// Grouped MX products with wide outputs take 4 slabs per wave (one set of
 // activation fragments serves 4 weight fragments) when that still leaves this
 // many waves: measured faster for the expert up product of a 64-token decode
 // (N = 5120), no better for N = 2048, and slower with bf16 weights.
@@ -81,6 +84,17 @@ __device__ __forceinline__ void split3_bf16x8(const u32x4 a, const u32x4 b, u32x
     part[q] = u32x4{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16), bits[4] | (bits[5] << 16),
                     bits[6] | (bits[7] << 16)};
   }
+}
+
+// 8 E2M1 codes (k order, lowest nibble first) times the block scale as one
+// bf16 MFMA operand: v_cvt_scalef32_pk_bf16_fp4 decodes the two codes of a
+// byte and scales them, exactly.
+__device__ __forceinline__ u32x4 mx4_decode8(uint32_t c, uint32_t s) {
+  const float sc = __uint_as_float(s == 0 ? 0x00400000u : (s << 23));
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3))};
 }
 
 int skinny_slabs_per_wave(const SkinnyProblem& P) {
@@ -121,7 +135,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[j][t] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-  constexpr bool MX = BMODE == kSkinnyMx, F32 = BMODE == kSkinnyF32;
+  constexpr bool MX = BMODE == kSkinnyMx, MX4 = BMODE == kSkinnyMx4, F32 = BMODE == kSkinnyF32;
   // what one lane loads for one slab in one step: bf16 weights (w[0..1]), MXFP8
   // codes (w[0], decoded at use) and their block scale, or fp32 weights (w[0..3])
   struct BRaw {
@@ -142,8 +156,8 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int64_t e0 = b_base + (int64_t)nrow[j] * S.ldb + (lo - seg_k0) + kl;
-        if constexpr (MX) {
-          cp[j] = P.mx_codes + e0;
+        if constexpr (MX || MX4) {
+          cp[j] = P.mx_codes + (MX4 ? e0 / 2 : e0);
           sp[j] = P.mx_scales + b_base / 32 + (int64_t)nrow[j] * (S.ldb / 32) + (lo - seg_k0 + kl) / 32;
         } else if constexpr (F32) {
           fp[j] = P.f32_b + e0;
@@ -155,6 +169,10 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
         BRaw r;
         if constexpr (MX) {
           r.w[0] = *reinterpret_cast<const u32x4*>(cp[j] + st * 64);
+          r.s = sp[j][st * 2];
+        } else if constexpr (MX4) {
+          const u32x2 c = *reinterpret_cast<const u32x2*>(cp[j] + st * 32);
+          r.w[0] = u32x4{c.x, c.y, 0u, 0u};
           r.s = sp[j][st * 2];
         } else if constexpr (F32) {
 #pragma unroll
@@ -189,6 +207,9 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
             if constexpr (MX) {
               w1 = mx_decode8(u32x2{b[j].w[0].z, b[j].w[0].w}, b[j].s);
               w0 = mx_decode8(u32x2{b[j].w[0].x, b[j].w[0].y}, b[j].s);
+            } else if constexpr (MX4) {
+              w1 = mx4_decode8(b[j].w[0].y, b[j].s);
+              w0 = mx4_decode8(b[j].w[0].x, b[j].s);
             }
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
@@ -268,7 +289,11 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
 // fixed epilogue of a grouped expert product (which also names up and down
 // apart in profiles).
 constexpr int unroll_steps(int mt, int nsb, int bmode) {
-  const int u = MOE_SKINNY_INFLIGHT / (nsb * mt * (bmode == kSkinnyMx ? 16 : bmode == kSkinnyF32 ? 64 : 32));
+  const bool mx = bmode == kSkinnyMx || bmode == kSkinnyMx4;
+  const int bytes = bmode == kSkinnyMx ? 16 : bmode == kSkinnyMx4 ? 8 : bmode == kSkinnyF32 ? 64 : 32;
+  int u = (mx ? MOE_SKINNY_MX_INFLIGHT : MOE_SKINNY_INFLIGHT) / (nsb * mt * bytes);
+  // the activation fragments of the steps in flight take 8 registers each per m-tile
+  if (u > 8 / mt) u = 8 / mt;
   return u > 0 ? u : 1;
 }
 
@@ -303,8 +328,8 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
   const int n_first = blk * 16 * NSB;
   const int epi = GROUPED_EPI >= 0 ? GROUPED_EPI : P.epi;
 
-  if constexpr (BMODE == kSkinnyMx) {
-    // MXFP8 experts: passes of 16 rows (an expert of a decode batch has a few;
+  if constexpr (BMODE == kSkinnyMx || BMODE == kSkinnyMx4) {
+    // MX experts: passes of 16 rows (an expert of a decode batch has a few;
     // more rows read its weights again). Keeping only the one-tile variant
     // leaves room for twice the codes in flight per lane at the same occupancy.
     for (int r0 = 0; r0 < rows; r0 += 16)
@@ -406,18 +431,24 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
     if (P.f32_b != nullptr) return hipErrorInvalidValue;        // fp32 weights: dense products only
     if (P.mx_codes != nullptr && P.nseg != 1) return hipErrorInvalidValue;
     const bool relu2 = P.epi == EPI_RELU2_BF16, mx = P.mx_codes != nullptr;
-    if (nsb == 4) {                                             // MXFP8 only, see skinny_slabs_per_wave
-      if (relu2) hipLaunchKernelGGL((skinny_kernel<4, EPI_RELU2_BF16, kSkinnyMx>), grid, block, 0, st, P);
-      else hipLaunchKernelGGL((skinny_kernel<4, EPI_BF16, kSkinnyMx>), grid, block, 0, st, P);
-    } else if (relu2 && mx) {
-      hipLaunchKernelGGL((skinny_kernel<1, EPI_RELU2_BF16, kSkinnyMx>), grid, block, 0, st, P);
+    const bool fp4 = mx && P.mx_fp4;
+#define MOE_GROUPED_MX(NS, FMT)                                                                             \
+  if (relu2) hipLaunchKernelGGL((skinny_kernel<NS, EPI_RELU2_BF16, FMT>), grid, block, 0, st, P);          \
+  else hipLaunchKernelGGL((skinny_kernel<NS, EPI_BF16, FMT>), grid, block, 0, st, P);
+    if (nsb == 4 && fp4) {                                      // MX only, see skinny_slabs_per_wave
+      MOE_GROUPED_MX(4, kSkinnyMx4)
+    } else if (nsb == 4) {
+      MOE_GROUPED_MX(4, kSkinnyMx)
+    } else if (fp4) {
+      MOE_GROUPED_MX(1, kSkinnyMx4)
+    } else if (mx) {
+      MOE_GROUPED_MX(1, kSkinnyMx)
     } else if (relu2) {
       hipLaunchKernelGGL((skinny_kernel<1, EPI_RELU2_BF16>), grid, block, 0, st, P);
-    } else if (mx) {
-      hipLaunchKernelGGL((skinny_kernel<1, EPI_BF16, kSkinnyMx>), grid, block, 0, st, P);
     } else {
       hipLaunchKernelGGL((skinny_kernel<1, EPI_BF16>), grid, block, 0, st, P);
     }
+#undef MOE_GROUPED_MX
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.partial == nullptr) return e;

@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 102
+    assert lib.moe_abi_version() == 103
 
 
 def test_status_strings(lib):
@@ -214,3 +214,16 @@ def test_block_entry_points_validate_before_any_launch(lib):
     assert b(256, 0, 1e-3, 256, None) == -1
     assert b(256, 8, float("nan"), 256, None) == -1
     assert b(256, 8, 1e-3, None, None) == -1
+
+
+def test_mxfp4_entry_points_validate_before_any_launch(lib):
+    q = lib.moe_quantize_mxfp4
+    assert q(256, 4, 48, 256, 256, None) == -1       # cols not a multiple of 32
+    assert q(256, 0, 64, 256, 256, None) == -1
+    assert q(None, 4, 64, 256, 256, None) == -1
+    assert q(264, 4, 64, 256, 256, None) == -1       # misaligned source
+    d = _d(TINY)
+    need = lib.moe_workspace_bytes(d)
+    w = M._Weights(*([256] * 3 + [0, 0] + [256] * 3))
+    bad = M._ExpertsMx(256, 256, 256, 256, 2)          # no format 2
+    assert lib.moe_forward_mx(d, ctypes.byref(w), ctypes.byref(bad), 256, 256, 256, need, None) == -1

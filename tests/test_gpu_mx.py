@@ -1,6 +1,6 @@
-"""MXFP8 expert weights on an MI355X: the quantiser against the oracle's, bit for
-bit, and the few-token forward on MXFP8 experts against the oracle run on the
-oracle's own dequantised experts.
+"""MX expert weights (MXFP8 and MXFP4) on an MI355X: the quantisers against the
+oracle's, bit for bit, and the few-token forward on MX experts against the
+oracle run on the oracle's own dequantised experts.
 
 Bars: codes and scales bit-exact; routing as in the bf16 forward; the layer
 output within max|err| / max|ref| <= 2e-2 of the oracle; and, since the kernels
@@ -36,16 +36,22 @@ def _exact_bf16_bits(v: np.ndarray) -> np.ndarray:
     return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def _oracle_mx(bits: np.ndarray):
-    """The oracle's MXFP8 codes, scales and dequantised bf16 bits of bf16 ``bits``."""
-    codes, scales = oracle.quantize_mxfp8(oracle.bf16_bits_to_f64(bits))
-    return codes, scales, _exact_bf16_bits(oracle.dequantize_mxfp8(codes, scales))
+_ORACLE_Q = {"mxfp8": (oracle.quantize_mxfp8, oracle.dequantize_mxfp8),
+             "mxfp4": (oracle.quantize_mxfp4, oracle.dequantize_mxfp4)}
+FORMATS = ["mxfp8", "mxfp4"]
 
 
-def _gpu_quant(bits: np.ndarray):
+def _oracle_mx(bits: np.ndarray, fmt="mxfp8"):
+    """The oracle's MX codes, scales and dequantised bf16 bits of bf16 ``bits``."""
+    q, dq = _ORACLE_Q[fmt]
+    codes, scales = q(oracle.bf16_bits_to_f64(bits))
+    return codes, scales, _exact_bf16_bits(dq(codes, scales))
+
+
+def _gpu_quant(bits: np.ndarray, fmt="mxfp8"):
     src = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-    log(f"[quantize] {tuple(bits.shape)}")
-    c, s = M.quantize_mxfp8(src)
+    log(f"[quantize] {fmt} {tuple(bits.shape)}")
+    c, s = (M.quantize_mxfp8 if fmt == "mxfp8" else M.quantize_mxfp4)(src)
     torch.cuda.synchronize()
     return c.cpu().numpy(), s.cpu().numpy()
 
@@ -55,7 +61,8 @@ def _finite_bf16_patterns() -> np.ndarray:
     return p[((p >> 7) & 0xFF) != 0xFF].astype(np.uint16)        # 65024 patterns, no inf / NaN
 
 
-def test_quantizer_every_finite_bf16_value():
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_quantizer_every_finite_bf16_value(fmt):
     pats = _finite_bf16_patterns()
     rng = np.random.default_rng(5)
     mags = oracle.bf16_bits_to_f64(pats)
@@ -64,33 +71,36 @@ def test_quantizer_every_finite_bf16_value():
         pats[np.argsort(np.abs(mags), kind="stable")],  # neighbours in magnitude: every scale, every code
     ]
     bits = np.concatenate(blocks).reshape(-1, 64)
-    c, s = _gpu_quant(bits)
-    rc, rs, _ = _oracle_mx(bits)
+    c, s = _gpu_quant(bits, fmt)
+    rc, rs, _ = _oracle_mx(bits, fmt)
     assert np.array_equal(s, rs), f"scales differ in {np.count_nonzero(s != rs)} blocks"
     bad = np.nonzero(c != rc)
     assert bad[0].size == 0, f"{bad[0].size} codes differ, first at {bad[0][0]},{bad[1][0]}"
 
 
-def test_quantizer_special_blocks():
-    f = np.zeros((6, 32))
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_quantizer_special_blocks(fmt):
+    f = np.zeros((7, 32))
     f[1] = -0.0                                               # negative zeros keep their sign bit
     f[2, 0] = 448.0 * 2 ** 3; f[2, 1:] = np.arange(1, 32) * 2 ** -7     # one large element, the rest tiny
     f[3] = np.linspace(-1, 1, 32)
     # ties of the E4M3 grid at scale 2^0 (block max 256..511): 1 + k/16 for odd k
     f[4, 0] = 256.0; f[4, 1:] = 1.0 + (2 * np.arange(31) % 16 + 1) / 16.0
     f[5, 0] = 2.0 ** -120; f[5, 1] = -(2.0 ** -121)          # tiny block: the scale exponent clamps at -127
+    # ties of the E2M1 grid at scale 2^0 (block max 6): halfway points of every step
+    f[6, 0] = 6.0; f[6, 1:15] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 2) * np.repeat([1, -1], 7)
     bits = _exact_bf16_bits(oracle.round_bf16(f))
-    c, s = _gpu_quant(bits)
-    rc, rs, _ = _oracle_mx(bits)
+    c, s = _gpu_quant(bits, fmt)
+    rc, rs, _ = _oracle_mx(bits, fmt)
     assert np.array_equal(s, rs) and np.array_equal(c, rc)
-    assert c[1].tolist() == [0x80] * 32
+    assert c[1].tolist() == ([0x80] * 32 if fmt == "mxfp8" else [0x88] * 16)   # negative zeros keep their sign
 
 
-def _quantize_experts(d, label):
-    """The GPU's MXFP8 experts and the oracle's, both quantised from the same bf16 weights."""
-    mx = M.quantize_experts_mxfp8(weights_of(d))
+def _quantize_experts(d, label, fmt="mxfp8"):
+    """The GPU's MX experts, quantised from the workload's bf16 weights."""
+    mx = M.quantize_experts_mx(weights_of(d), fmt)
     torch.cuda.synchronize()
-    log(f"[quantize] {label} experts on the GPU")
+    log(f"[quantize] {label} experts on the GPU ({fmt})")
     return mx
 
 
@@ -98,13 +108,13 @@ class _OracleExperts:
     """expert(e) for the oracle: the oracle's dequantised MXFP8 weights of expert e,
     after checking that the GPU's codes and scales of that expert equal the oracle's."""
 
-    def __init__(self, d, mx):
-        self.d, self.mx, self.cache = d, mx, {}
+    def __init__(self, d, mx, fmt="mxfp8"):
+        self.d, self.mx, self.fmt, self.cache = d, mx, fmt, {}
 
     def _one(self, e):
         out = []
         for n in ("w_up", "w_down"):
-            c, s, deq = _oracle_mx(u16(self.d[n][e]))
+            c, s, deq = _oracle_mx(u16(self.d[n][e]), self.fmt)
             assert np.array_equal(self.mx[n + "_scale"][e].cpu().numpy(), s), f"{n}[{e}] scales"
             assert np.array_equal(self.mx[n][e].cpu().numpy(), c), f"{n}[{e}] codes"
             out.append(deq)
@@ -150,12 +160,13 @@ def _compare(d, out, idx, tokens, experts, label):
     assert e < OUT_TOL, f"{label}: max|err|/max|ref| = {e:.3g}"
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("over", [{}, dict(T=37), dict(T=1), dict(K=16), dict(K=1)])
-def test_forward_mx_tiny(over):
+def test_forward_mx_tiny(over, fmt):
     d = device_inputs("tiny", **over)
     cfg = d["cfg"]
-    mx = _quantize_experts(d, f"tiny{over}")
-    experts = _OracleExperts(d, mx)
+    mx = _quantize_experts(d, f"tiny{over}", fmt)
+    experts = _OracleExperts(d, mx, fmt)
     experts.prefetch(range(cfg.E))                 # every expert's codes checked against the oracle's
     out, idx, gate, gap = _run_mx(d, mx)
     check_routing(idx, gate, gap, oracle_route(d), label="tiny mx")
@@ -171,15 +182,16 @@ def test_forward_mx_tiny(over):
 
 
 @pytest.mark.timeout(400)
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("name", ["ultra_decode1", "ultra_decode64"])
-def test_forward_mx_ultra(name):
+def test_forward_mx_ultra(name, fmt):
     d = device_inputs(name)
     cfg = d["cfg"]
-    mx = _quantize_experts(d, name)
+    mx = _quantize_experts(d, name, fmt)
     out, idx, gate, gap = _run_mx(d, mx)
     check_routing(idx, gate, gap, oracle_route(d), label=f"{name} mx")
     # the last token (the ragged end of the batch); its experts' codes are checked bit for bit
-    _compare(d, out, idx, np.array([cfg.T - 1]), _OracleExperts(d, mx), name)
+    _compare(d, out, idx, np.array([cfg.T - 1]), _OracleExperts(d, mx, fmt), f"{name} {fmt}")
 
 
 def test_forward_mx_rejects_many_tokens():
