@@ -147,7 +147,9 @@ def _check_epilogue_exact(d, out, xn):
 
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", dict(T=37)), ("tiny", dict(T=1)),
-                                       ("tiny", dict(T=300)), ("tiny", dict(T=777, K=1))])
+                                       ("tiny", dict(T=300)), ("tiny", dict(T=777, K=1)),
+                                       ("tiny", dict(T=333, H=320, L=192, E=24, I=448, Is=576, K=5)),
+                                       ("tiny", dict(T=29, H=320, L=192, E=24, I=448, Is=576, K=5))])
 def test_block_tiny_full(name, over):
     d = device_inputs(name, **over)
     cfg = d["cfg"]

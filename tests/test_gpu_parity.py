@@ -214,7 +214,13 @@ def _compare_tokens(d, out, ws, lay, tokens, idx_gpu, label):
                                        ("tiny", dict(K=16)), ("tiny", dict(K=1)),
                                        # above the few-token threshold: the tiled GEMM path
                                        ("tiny", dict(T=300)), ("tiny", dict(T=65, K=16)),
-                                       ("tiny", dict(T=777, K=1))])
+                                       ("tiny", dict(T=777, K=1)),
+                                       # widths that are multiples of 64 but not of the 256-wide
+                                       # tiles: ragged column tiles in every product, both paths
+                                       ("tiny", dict(T=333, H=320, L=192, E=24, I=448, Is=576, K=5)),
+                                       ("tiny", dict(T=29, H=320, L=192, E=24, I=448, Is=576, K=5)),
+                                       # one expert: every token's one slot goes to it
+                                       ("tiny", dict(T=300, E=1, K=1)), ("tiny", dict(T=7, E=1, K=1))])
 def test_forward_tiny_full(name, over):
     d = device_inputs(name, **over)
     cfg = d["cfg"]
