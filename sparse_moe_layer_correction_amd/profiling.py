@@ -76,12 +76,12 @@ def _per_dispatch(counter_csv: str, counter: str):
 
 # which kernel a phase of the forward launches, by the order bench.py's profiled
 # step runs them (grouped launches carry their epilogue in the name)
-# (the few-token kernels: <slabs per wave, epilogue, weight format 0 bf16 / 1 MXFP8>)
+# (the few-token kernels: <slabs per wave, epilogue, weight format 0 bf16 / 1 MXFP8 / 3 MXFP4>)
 PHASE_KERNELS = {
-    "expert_up": (r"gemm_bf16_kernel<256, 256, 2, 2, 1, 1>", r"skinny_kernel<1, 1, 0>",
-                  r"skinny_kernel<1, 1, 1>", r"skinny_kernel<4, 1, 1>"),
-    "expert_down": (r"gemm_bf16_kernel<256, 256, 2, 2, 0, 1>", r"skinny_kernel<1, 0, 0>",
-                    r"skinny_kernel<1, 0, 1>", r"skinny_kernel<4, 0, 1>"),
+    "expert_up": (r"gemm_bf16_kernel<256, 256, 2, 2, 1, 1>",) +
+                 tuple(f"skinny_kernel<{ns}, 1, {f}>" for ns in (1, 4) for f in (0, 1, 3)),
+    "expert_down": (r"gemm_bf16_kernel<256, 256, 2, 2, 0, 1>",) +
+                   tuple(f"skinny_kernel<{ns}, 0, {f}>" for ns in (1, 4) for f in (0, 1, 3)),
 }
 
 
