@@ -264,7 +264,7 @@ size_t moe_block_workspace_bytes(const moe_dims* dims);
  * scratch; its moe_ws_layout offsets are unchanged) and the residual add runs
  * in the epilogue of the final product: fc2 + shared down are rounded to bf16,
  * added to x in fp32 and rounded once more. mx: NULL for the bf16 experts of
- * `w`, else MXFP8 experts as for moe_forward_mx (T <= 64). out may equal x
+ * `w`, else MX experts as for moe_forward_mx (T <= 64). out may equal x
  * (every element of x is read before the same element of out is written).
  * Errors as moe_forward, plus MOE_ERR_INVALID for a null or misaligned gamma
  * or x, or a bad eps; MOE_ERR_WORKSPACE below moe_block_workspace_bytes. */

@@ -271,7 +271,7 @@ _WEIGHT_SPECS = ("w_router", "corr_bias", "w_fc1", "w_up", "w_down", "w_fc2", "w
 
 
 def _weight_struct(dims: MoEDims, w: Dict, dev, experts: bool = True):
-    """experts=False: the bf16 expert weights are not needed (MXFP8 experts given apart)."""
+    """experts=False: the bf16 expert weights are not needed (MX experts given apart)."""
     torch = _torch()
     H, L, E, I, Is = dims.H, dims.L, dims.E, dims.I, dims.Is
     shapes = {"w_router": ((E, H), torch.float32), "corr_bias": ((E,), torch.float32),
@@ -286,7 +286,7 @@ def _weight_struct(dims: MoEDims, w: Dict, dev, experts: bool = True):
 
 
 # ----------------------------------------------------------------------------
-# MXFP8 expert weights
+# MX (MXFP8 / MXFP4) expert weights
 # ----------------------------------------------------------------------------
 
 def quantize_mxfp8(w, *, stream=None):
@@ -354,7 +354,7 @@ def dims_from_mx(x, weights: Dict, mx: Dict, K: int, routed_scaling: float = 5.0
 
 def forward_mx(x, weights: Dict, mx: Dict, K: int, routed_scaling: float = 5.0, *, out=None, ws=None,
                stream=None, n_group: int = 1, topk_group: int = 1):
-    """moe_forward_mx: the forward with MXFP8 expert weights ``mx`` (T <= 64)."""
+    """moe_forward_mx: the forward with MX expert weights ``mx`` (quantize_experts_mx; T <= 64)."""
     torch = _torch()
     dims = dims_from_mx(x, weights, mx, K, routed_scaling, n_group, topk_group)
     dev = x.device
@@ -453,7 +453,7 @@ def block_workspace_bytes(dims: MoEDims) -> int:
 
 def block_forward(x, weights: Dict, gamma, K: int, routed_scaling: float = 5.0, eps: float = RMS_EPS, *, mx=None,
                   out=None, ws=None, stream=None, n_group: int = 1, topk_group: int = 1):
-    """moe_block_forward: out = x + LatentMoE(RMSNorm(x)); ``mx`` optional MXFP8 experts (T <= 64).
+    """moe_block_forward: out = x + LatentMoE(RMSNorm(x)); ``mx`` optional MX experts (T <= 64).
     ``out`` may be ``x`` (in place)."""
     torch = _torch()
     if mx is None:

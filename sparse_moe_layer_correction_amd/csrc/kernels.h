@@ -38,7 +38,7 @@ struct SkinnyProblem {
   int epi;
   int ksplit;                // dense: K split over this many waves per slab
   float* partial;            // [ksplit, M, N] fp32 when ksplit > 1, else null
-  // MXFP8 weights (grouped products, one K segment): when set, B comes from
+  // MX weights (grouped products, one K segment): when set, B comes from
   // E4M3 codes [.., N, K] (b_estride apart per expert, row length seg[0].ldb)
   // and E8M0 scales, one per 32 k; seg[0].B is then unused
   const uint8_t* mx_codes;
@@ -51,7 +51,7 @@ struct SkinnyProblem {
   const uint16_t* residual;
   int64_t ldr;
 };
-// the weight operand of a skinny product: bf16, MXFP8 codes and scales, or fp32
+// the weight operand of a skinny product: bf16, MXFP8 or MXFP4 codes and scales, or fp32
 enum SkinnyBMode : int { kSkinnyBf16 = 0, kSkinnyMx = 1, kSkinnyF32 = 2, kSkinnyMx4 = 3 };
 hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st);
 hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t nblocks, uint8_t* codes, uint8_t* scales,

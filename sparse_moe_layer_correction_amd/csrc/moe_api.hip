@@ -360,7 +360,7 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* s
 
 namespace {
 
-// mx: MXFP8 expert weights (then w->w_up / w->w_down are not read), or null.
+// mx: MX (MXFP8 or MXFP4) expert weights (then w->w_up / w->w_down are not read), or null.
 // The block around the layer: x_in is normed into the workspace (after the
 // layer's own scratch) and is the residual of the output.
 struct BlockArgs {

@@ -3,9 +3,10 @@
 // MXFP4 (E2M1 elements, two per byte).
 //
 // The released model keeps its experts in a block-scaled 4-bit format (the QA
-// page on the experts' NVFP4 storage); MXFP8 is the block-scaled format whose
-// decode gfx950 does in one instruction per two elements. Per block: the shared
-// exponent is e = floor(log2(max |v|)) - 8 (8 = the exponent of E4M3's largest
+// page on the experts' NVFP4 storage); MXFP8 and MXFP4 are the block-scaled
+// formats whose decode gfx950 does in one instruction per two elements.
+//
+// MXFP8. Per block: the shared exponent is e = floor(log2(max |v|)) - 8 (8 = the exponent of E4M3's largest
 // normal, 448), clamped to [-127, 127], stored as the code e + 127 (an all-zero
 // block takes e = -127); each element is v * 2^-e rounded to the nearest E4M3
 // value, ties to even, magnitudes of 448 and above saturating to 448 (E4M3 "fn"

@@ -17,7 +17,7 @@
 // the partials in a fixed order and applies the epilogue, so results do not
 // depend on timing. Grouped products (experts) need no split: a slab of one
 // expert covers its rows, and there are E x N/16 slabs. Their weights may also
-// come as MXFP8 (E4M3 codes with a power-of-two scale per 32 k), decoded to
+// come as MXFP8 or MXFP4 (E4M3 / E2M1 codes with a power-of-two scale per 32 k), decoded to
 // bf16 in registers on the way to the MFMA: half the bytes of bf16 weights.
 #include "kernels.h"
 
@@ -107,8 +107,8 @@ int skinny_slabs_per_wave(const SkinnyProblem& P) {
 // in 64-deep steps of two 16x16x32 MFMAs; in each step lane group g = lane/16
 // holds k = 16g .. 16g+15 of the step (the first MFMA takes its low 8, the
 // second its high 8), so a lane's weights of a step are 16 consecutive
-// elements: two 16-byte loads of bf16, or one 16-byte load of MXFP8 codes plus
-// the one scale byte they share, or four 16-byte loads of fp32 weights (the
+// elements: two 16-byte loads of bf16, one 16-byte (MXFP8) or 8-byte (MXFP4)
+// load of codes plus the one scale byte they share, or four 16-byte loads of fp32 weights (the
 // router's), each split exactly into three bf16 parts hi + mid + lo that take
 // one MFMA each. The activations are loaded in the same k order, so the
 // products are unchanged; per step the wave issues MT*NS*2 MFMAs (three times
@@ -136,8 +136,8 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
     for (int t = 0; t < MT; ++t) acc[j][t] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
   constexpr bool MX = BMODE == kSkinnyMx, MX4 = BMODE == kSkinnyMx4, F32 = BMODE == kSkinnyF32;
-  // what one lane loads for one slab in one step: bf16 weights (w[0..1]), MXFP8
-  // codes (w[0], decoded at use) and their block scale, or fp32 weights (w[0..3])
+  // what one lane loads for one slab in one step: bf16 weights (w[0..1]), MX codes
+  // (w[0], decoded at use) and their block scale, or fp32 weights (w[0..3])
   struct BRaw {
     u32x4 w[4];
     uint32_t s;
@@ -417,7 +417,7 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
   if (tasks <= 0) return hipSuccess;
   const dim3 grid((unsigned)((tasks + 3) / 4)), block(256);
   if (P.offsets == nullptr) {
-    if (P.mx_codes != nullptr) return hipErrorInvalidValue;     // MXFP8 weights: grouped products only
+    if (P.mx_codes != nullptr) return hipErrorInvalidValue;     // MX weights: grouped products only
     if (P.f32_b != nullptr) {                                   // fp32 weights: one K segment
       if (P.nseg != 1) return hipErrorInvalidValue;
       if (nsb == 4) hipLaunchKernelGGL((skinny_kernel<4, -1, kSkinnyF32>), grid, block, 0, st, P);
