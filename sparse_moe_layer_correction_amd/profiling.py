@@ -32,11 +32,19 @@ FAMILIES = {"gemm": ("gemm.h", "common.h"), "skinny": ("skinny.hip", "common.h")
 CALIBRATION_BYTES = 1 << 30
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank-line or trailing-space differences."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(family: str) -> str:
+    """Hash of the code (comments left out) of the sources a kernel family is built from."""
     h = hashlib.sha256()
     for f in FAMILIES[family]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
