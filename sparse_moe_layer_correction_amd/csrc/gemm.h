@@ -269,7 +269,9 @@ gemm_bf16_kernel(const GemmLaunch L) {
       if constexpr (decltype(st)::value == 0) return sb0;
       else return sb1;
     };
-    auto issue = [&](int kt, auto st, bool live = true) {
+    // loads of a tile in four quarters: bit 0 / 1 the first / second half of a
+    // thread's A loads, bit 2 / 3 the same for B
+    auto issue = [&](int kt, auto st, bool live = true, int parts = 15) {
       while (kt >= seg_end) {          // uniform; at most nseg-1 times in the whole loop
         seg_k0 = seg_end;
         ++seg;
@@ -285,10 +287,14 @@ gemm_bf16_kernel(const GemmLaunch L) {
       u32x4* b = stB(st);
   #pragma unroll
       for (int i = 0; i < NAX; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)&a[(wave * NAX + i) * 64], 16, (int)ao[i], so, 0, 0);
+        if (parts & (i < NAX / 2 ? 1 : 2))
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)&a[(wave * NAX + i) * 64], 16, (int)ao[i], so, 0,
+                                                   0);
   #pragma unroll
       for (int i = 0; i < NB; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)&b[(wave * NB + i) * 64], 16, (int)bo[i], so, 0, 0);
+        if (parts & (i < NB / 2 ? 4 : 8))
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)&b[(wave * NB + i) * 64], 16, (int)bo[i], so, 0,
+                                                   0);
     };
 
     // Fragments of one 16-deep k substep: lane l reads row (l & 31) of each
@@ -334,14 +340,36 @@ gemm_bf16_kernel(const GemmLaunch L) {
     // substep runs and the first fragments of tile kt+1 are read.
     constexpr int NM = TMX * TN, NR = TMX + TN;
     Frag f0, f1;
+    // When each quarter of tile kt+2's loads is issued (plan digits for A lo, A hi,
+    // B lo, B hi: 3 = after the barrier of step kt, 0 / 1 = in the first / second
+    // substep of step kt+1). All at the barrier left the waves' load issue in one
+    // burst that put them out of step (the barrier then waits for the slowest):
+    // spreading the B half over the next tile's first substeps took 3-6 % off
+    // every product on the Ultra prefill, the best split differing by product.
+    constexpr int PLAN = EPI == EPI_RELU2_BF16 ? 3300 : 3301;
+    constexpr int QD[4] = {PLAN / 1000, PLAN / 100 % 10, PLAN / 10 % 10, PLAN % 10};
+    constexpr int QN[4] = {NAX / 2, NAX - NAX / 2, NB / 2, NB - NB / 2};
+    constexpr int M0 = (QD[0] == 0) | (QD[1] == 0) << 1 | (QD[2] == 0) << 2 | (QD[3] == 0) << 3;
+    constexpr int M1 = (QD[0] == 1) | (QD[1] == 1) << 1 | (QD[2] == 1) << 2 | (QD[3] == 1) << 3;
+    constexpr int M3 = (QD[0] == 3) | (QD[1] == 3) << 1 | (QD[2] == 3) << 2 | (QD[3] == 3) << 3;
+    constexpr int N0 = (M0 & 1 ? QN[0] : 0) + (M0 & 2 ? QN[1] : 0) + (M0 & 4 ? QN[2] : 0) + (M0 & 8 ? QN[3] : 0);
+    constexpr int N1 = (M1 & 1 ? QN[0] : 0) + (M1 & 2 ? QN[1] : 0) + (M1 & 4 ? QN[2] : 0) + (M1 & 8 ? QN[3] : 0);
+    constexpr int N3 = (M3 & 1 ? QN[0] : 0) + (M3 & 2 ? QN[1] : 0) + (M3 & 4 ? QN[2] : 0) + (M3 & 8 ? QN[3] : 0);
     auto step = [&](int kt, auto st) {
       constexpr int S = decltype(st)::value;
       read(f1, st, 1);
+      // quarters of tile kt+1 (in the other stage) planned for this substep
+      if constexpr (M0 != 0) {
+        if (kt >= 1) issue(min(kt + 1, nk - 1), Stage<1 - S>{}, kt + 1 < nk, M0);
+      }
       mma(f0);
-      interleave<NM, NR, 0>();
+      interleave<NM, NR, N0>();
       read(f0, st, 2);
+      if constexpr (M1 != 0) {
+        if (kt >= 1) issue(min(kt + 1, nk - 1), Stage<1 - S>{}, kt + 1 < nk, M1);
+      }
       mma(f1);
-      interleave<NM, NR, 0>();
+      interleave<NM, NR, N1>();
       read(f1, st, 3);
       mma(f0);
       interleave<NM, NR, 0>();
@@ -349,10 +377,10 @@ gemm_bf16_kernel(const GemmLaunch L) {
       __builtin_amdgcn_sched_barrier(0);
       // past the end the load still runs (the schedule stays the same) but over
       // an empty range, so it moves no data and lands at once
-      issue(min(kt + 2, nk - 1), st, kt + 2 < nk);
+      if constexpr (M3 != 0) issue(min(kt + 2, nk - 1), st, kt + 2 < nk, M3);
       read(f0, Stage<1 - S>{}, 0);
       mma(f1);
-      interleave<NM, NR, NAX + NB>();
+      interleave<NM, NR, N3>();
     };
 
     issue(0, Stage<0>{});
