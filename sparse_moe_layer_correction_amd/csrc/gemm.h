@@ -50,7 +50,6 @@ struct GemmProblem {
   const int32_t* gather;     // nullable: A row of output row r is gather[r]
   const int32_t* tile_e;     // nullable: grouped mode tile table (expert of M tile);
                              //   a grouped launch holds exactly one problem
-  const int32_t* tile_m0;    //   first permuted row of M tile
   const int32_t* n_mtiles;   //   device scalar: number of valid M tiles
   const int32_t* first_mtile;  // [E] each expert's first M tile in the table
   const int32_t* offsets;    //   [E+1] expert row offsets
@@ -171,7 +170,8 @@ gemm_bf16_kernel(const GemmLaunch L) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave % WM, wave_n = wave / WM;
 
-  int mt, nt, pi = 0;
+  int pi = 0, m0, mend, n0;
+  int64_t b_base = 0;
   if (L.p[0].tile_e != nullptr) {
     // grouped: the grid is sized for the most M tiles any routing can need; only
     // the first n_mtiles * ntiles workgroups work, and the XCD renumbering runs
@@ -182,32 +182,29 @@ gemm_bf16_kernel(const GemmLaunch L) {
     if ((int)blockIdx.x >= valid) return;
     // expert by expert: the tiles of one expert are contiguous in the order,
     // M fastest, so the M tiles that share a weight panel run side by side
+    // (an expert's ne M tiles times ntl N tiles are contiguous in t, starting at
+    // first_mtile[e] * ntl, so t / ntl lands on one of the expert's own M tiles;
+    // its tiles start at its first permuted row, offsets[e], BM rows apart).
+    // Every table read here is one dependent step of the workgroup's start.
     const int t = xcd_remap(blockIdx.x, valid);
     const int e = L.p[0].tile_e[t / ntl];
     const int f = L.p[0].first_mtile[e];
-    const int ne = (L.p[0].offsets[e + 1] - L.p[0].offsets[e] + BM - 1) / BM;
+    const int o0 = L.p[0].offsets[e], o1 = L.p[0].offsets[e + 1];
+    const int ne = (o1 - o0 + BM - 1) / BM;
     const int local = t - f * ntl;
-    mt = f + local % ne;
-    nt = local / ne;
+    m0 = o0 + (local % ne) * BM;
+    mend = o1;
+    n0 = (local / ne) * BN;
+    b_base = (int64_t)e * L.p[0].b_estride;
   } else {
     int bid = xcd_remap(blockIdx.x, gridDim.x);
     if (L.np > 1 && bid >= L.tiles0) { pi = 1; bid -= L.tiles0; }
+    int mt, nt;
     tile_order(bid, L.p[pi].mtiles, L.p[pi].ntiles, L.p[pi].group_m, mt, nt);
-  }
-  const GemmProblem& Q = L.p[pi];
-
-  int m0, mend;
-  int64_t b_base = 0;
-  if (Q.tile_e != nullptr) {
-    const int e = Q.tile_e[mt];
-    m0 = Q.tile_m0[mt];
-    mend = Q.offsets[e + 1];
-    b_base = (int64_t)e * Q.b_estride;
-  } else {
     m0 = mt * BM;
-    mend = Q.M;
+    mend = L.p[pi].M;
+    n0 = nt * BN;
   }
-  const int n0 = nt * BN;
 
   // In the grouped products (the instantiations with a fixed epilogue), an
   // expert's tail tile with at most BM/2 valid rows runs the half path: the same
@@ -444,22 +441,36 @@ gemm_bf16_kernel(const GemmLaunch L) {
               u32x2{cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3)};
         }
     }
-    // read back: 64 / CPW rows per instruction, CPW lanes per row
-    constexpr int RPI = 64 / CPW;
+    // read back: 64 / CPW rows per instruction, CPW lanes per row. The problem's
+    // fields are copied first: read through P after a store, the compiler would
+    // load them again (it cannot tell the stores from the kernel arguments),
+    // and each such reload serialised one read-back and store.
+    constexpr int RPI = 64 / CPW, NRB = WTMX / RPI;
+    const int Nc = P.N;
+    const int64_t ldc = P.ldc, ldr = P.ldr;
+    uint16_t* const Cp = static_cast<uint16_t*>(P.C);
+    const uint16_t* const res = EPI < 0 ? P.residual : nullptr;
+    u32x4 rb[NRB];
 #pragma unroll
-    for (int i = 0; i < WTMX / RPI; ++i) {
+    for (int i = 0; i < NRB; ++i) {
       const int r = i * RPI + lane / CPW;
       const int c = lane % CPW;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (CPW * 16) + ((c ^ (r % CPW)) * 16));
+      rb[i] = *reinterpret_cast<const u32x4*>(stg + r * (CPW * 16) + ((c ^ (r % CPW)) * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      const int r = i * RPI + lane / CPW;
+      const int c = lane % CPW;
+      const u32x4 v = rb[i];
       const int m = m0 + wave_m * WTMX + r;
       const int n = n0 + wave_n * WTN + c * 8;
-      if (m >= mend || n >= P.N) continue;
-      uint16_t* dst = static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n;
-      const bool full = n + 8 <= P.N;                 // else 4 columns (N is a multiple of 4)
+      if (m >= mend || n >= Nc) continue;
+      uint16_t* dst = Cp + (int64_t)m * ldc + n;
+      const bool full = n + 8 <= Nc;                  // else 4 columns (N is a multiple of 4)
       u32x4 o = v;
-      if (EPI < 0 && P.residual != nullptr) {
+      if (EPI < 0 && res != nullptr) {
         // the block's residual add: bf16 + bf16 in fp32 (exact), rounded once
-        const uint16_t* src = P.residual + (int64_t)m * P.ldr + n;
+        const uint16_t* src = res + (int64_t)m * ldr + n;
         u32x4 rv;
         if (full) rv = *reinterpret_cast<const u32x4*>(src);
         else {

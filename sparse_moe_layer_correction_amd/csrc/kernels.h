@@ -65,7 +65,6 @@ struct PermuteScratch {
   int32_t* base;       // [E][nblk]
   int32_t* counts;     // [E]
   int32_t* tile_e;     // [max_mtiles]
-  int32_t* tile_m0;    // [max_mtiles]
   int32_t* n_mtiles;   // [1]
   int32_t* touched;    // [E] experts with at least one token, ascending
   int32_t* n_touched;  // [1]

@@ -41,7 +41,7 @@ struct Layout {
   // route
   size_t wsplit, logits;
   // permute
-  size_t masks, base, counts, tile_e, tile_m0, n_mtiles, touched, n_touched, first_mtile;
+  size_t masks, base, counts, tile_e, n_mtiles, touched, n_touched, first_mtile;
   // forward
   size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial;
   size_t route_end, permute_begin, permute_end, total;
@@ -106,7 +106,6 @@ Layout make_layout(const moe_dims& d) {
   l.base = take(E * l.nblk * 4);
   l.counts = take(E * 4);
   l.tile_e = take((size_t)l.max_mtiles * 4);
-  l.tile_m0 = take((size_t)l.max_mtiles * 4);
   l.n_mtiles = take(4);
   l.touched = take(E * 4);
   l.n_touched = take(4);
@@ -261,7 +260,7 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
 PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
   return PermuteScratch{at<uint64_t>(ws, l.masks - origin), at<int32_t>(ws, l.base - origin),
                         at<int32_t>(ws, l.counts - origin),   at<int32_t>(ws, l.tile_e - origin),
-                        at<int32_t>(ws, l.tile_m0 - origin),  at<int32_t>(ws, l.n_mtiles - origin),
+                        at<int32_t>(ws, l.n_mtiles - origin),
                         at<int32_t>(ws, l.touched - origin),  at<int32_t>(ws, l.n_touched - origin),
                         at<int32_t>(ws, l.first_mtile - origin)};
 }
@@ -474,7 +473,6 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.Nb = d.I;
     p.gather = row_token;
     p.tile_e = ps.tile_e;
-    p.tile_m0 = ps.tile_m0;
     p.n_mtiles = ps.n_mtiles;
     p.first_mtile = ps.first_mtile;
     p.offsets = offsets;
@@ -505,7 +503,6 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.N = d.L;
     p.Nb = d.L;
     p.tile_e = ps.tile_e;
-    p.tile_m0 = ps.tile_m0;
     p.n_mtiles = ps.n_mtiles;
     p.first_mtile = ps.first_mtile;
     p.offsets = offsets;

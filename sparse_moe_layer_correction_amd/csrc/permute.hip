@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(256) expert_scan_kernel(const uint64_t* __rest
 // the experts that received at least one token, in ascending order. Returns
 // the exclusive offset of expert tid.
 __device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __restrict__ offsets,
-                                              int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_m0,
+                                              int32_t* __restrict__ tile_e,
                                               int32_t* __restrict__ n_mtiles, int32_t* __restrict__ touched,
                                               int32_t* __restrict__ n_touched, int32_t* __restrict__ first_mtile) {
   __shared__ int wsum_c[16], wsum_t[16], wsum_h[16];
@@ -73,10 +73,7 @@ __device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __r
   if (tid < E) {
     offsets[tid] = ex_c;
     first_mtile[tid] = ex_t;
-    for (int i = 0; i < nt; ++i) {
-      tile_e[ex_t + i] = tid;
-      tile_m0[ex_t + i] = ex_c + i * BM;
-    }
+    for (int i = 0; i < nt; ++i) tile_e[ex_t + i] = tid;
     if (hit) touched[ex_h] = tid;
   }
   if (tid == E - 1) {
@@ -90,13 +87,12 @@ __device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __r
 __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict__ counts, int E, int BM,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ tile_e,
-                                                       int32_t* __restrict__ tile_m0,
                                                        int32_t* __restrict__ n_mtiles,
                                                        int32_t* __restrict__ touched,
                                                        int32_t* __restrict__ n_touched,
                                                        int32_t* __restrict__ first_mtile) {
   const int c = (int)threadIdx.x < E ? counts[threadIdx.x] : 0;
-  layout_experts(c, E, BM, offsets, tile_e, tile_m0, n_mtiles, touched, n_touched, first_mtile);
+  layout_experts(c, E, BM, offsets, tile_e, n_mtiles, touched, n_touched, first_mtile);
 }
 
 // All of steps 1-4 in one workgroup when the tokens fit one 64-token block
@@ -105,7 +101,6 @@ __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict
 __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx, int T, int K, int E,
                                                              int BM, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ tile_e,
-                                                             int32_t* __restrict__ tile_m0,
                                                              int32_t* __restrict__ n_mtiles,
                                                              int32_t* __restrict__ touched,
                                                              int32_t* __restrict__ n_touched,
@@ -124,7 +119,7 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
   }
   __syncthreads();
   const int c = tid < E ? __popcll(m[tid]) : 0;
-  const int ex = layout_experts(c, E, BM, offsets, tile_e, tile_m0, n_mtiles, touched, n_touched, first_mtile);
+  const int ex = layout_experts(c, E, BM, offsets, tile_e, n_mtiles, touched, n_touched, first_mtile);
   if (tid < E) off[tid] = ex;
   __syncthreads();
   for (int s = tid; s < tk; s += blockDim.x) {
@@ -177,12 +172,12 @@ hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, 
   const int nblk = (T + 63) / 64;
   if (nblk == 1) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, T, K, E, BM, offsets, ps.tile_e,
-                       ps.tile_m0, ps.n_mtiles, ps.touched, ps.n_touched, ps.first_mtile, row_token, slot_row);
+                       ps.n_mtiles, ps.touched, ps.n_touched, ps.first_mtile, row_token, slot_row);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(block_masks_kernel, dim3(nblk), dim3(256), 0, st, idx, T, K, E, nblk, ps.masks);
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, st, ps.masks, nblk, E, ps.base, ps.counts);
-  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, ps.counts, E, BM, offsets, ps.tile_e, ps.tile_m0,
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, ps.counts, E, BM, offsets, ps.tile_e,
                      ps.n_mtiles, ps.touched, ps.n_touched, ps.first_mtile);
   const int64_t tk = (int64_t)T * K;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st, idx, T, K, E, nblk,
