@@ -152,28 +152,30 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
       const uint16_t* bp[NS];
       const uint8_t* cp[NS];                 // MX: codes and the block scale of this lane's k
       const uint8_t* sp[NS];
+      const uint8_t* sq[NS];                 // MX: the scale row at the segment's first k
       const float* fp[NS];                   // fp32 weights
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int64_t e0 = b_base + (int64_t)nrow[j] * S.ldb + (lo - seg_k0) + kl;
         if constexpr (MX || MX4) {
           cp[j] = P.mx_codes + (MX4 ? e0 / 2 : e0);
-          sp[j] = P.mx_scales + b_base / 32 + (int64_t)nrow[j] * (S.ldb / 32) + (lo - seg_k0 + kl) / 32;
+          sq[j] = P.mx_scales + b_base / 32 + (int64_t)nrow[j] * (S.ldb / 32) + (lo - seg_k0) / 32;
+          sp[j] = sq[j] + kl / 32;
         } else if constexpr (F32) {
           fp[j] = P.f32_b + e0;
         } else {
           bp[j] = S.B + e0;
         }
       }
-      auto load_b = [&](int j, int st) -> BRaw {
+      auto load_b = [&](int j, int st, bool scale = true) -> BRaw {
         BRaw r;
         if constexpr (MX) {
           r.w[0] = *reinterpret_cast<const u32x4*>(cp[j] + st * 64);
-          r.s = sp[j][st * 2];
+          if (scale) r.s = sp[j][st * 2];
         } else if constexpr (MX4) {
           const u32x2 c = *reinterpret_cast<const u32x2*>(cp[j] + st * 32);
           r.w[0] = u32x4{c.x, c.y, 0u, 0u};
-          r.s = sp[j][st * 2];
+          if (scale) r.s = sp[j][st * 2];
         } else if constexpr (F32) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) r.w[q] = *reinterpret_cast<const u32x4*>(fp[j] + st * 64 + 4 * q);
@@ -224,14 +226,48 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
         }
       };
       const int nsteps = (hi - lo) / 64;
+      // MX scales of UNROLL steps in one load: a step takes two scale bytes of
+      // a row (lane group g the (g >> 1)-th), so a row's scales of the UNROLL
+      // steps are 2 * UNROLL consecutive bytes, shared by the lane's four lane
+      // groups; one byte load per step instead touched the 16 rows' lines
+      // every step. Used when those bytes are aligned for the wide load.
+      constexpr int SB = 2 * UNROLL;           // scale bytes of UNROLL steps
+      constexpr bool kScaleBlock = (MX || MX4) && (UNROLL == 4 || UNROLL == 8);
+      bool sblock = false;
+      if constexpr (kScaleBlock) {
+        bool al = (S.ldb / 32) % SB == 0 && ((lo - seg_k0) / 32) % SB == 0 && (b_base / 32) % SB == 0 &&
+                  (reinterpret_cast<uintptr_t>(P.mx_scales) & (SB - 1)) == 0;
+        sblock = al;
+      }
+      const int sh = (lane >> 5) * 8;          // lane group g = lane / 16 takes byte g >> 1 of a step's pair
       int st = 0;
       for (; st + UNROLL <= nsteps; st += UNROLL) {
         BRaw bv[UNROLL][NS];
         u32x4 a0[UNROLL][MT], a1[UNROLL][MT];
+        if (kScaleBlock && sblock) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+          for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-          for (int j = 0; j < NS; ++j) bv[u][j] = load_b(j, st + u);
+            for (int j = 0; j < NS; ++j) bv[u][j] = load_b(j, st + u, false);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            uint32_t w[4];
+            if constexpr (SB == 16) {
+              const u32x4 v = *reinterpret_cast<const u32x4*>(sq[j] + st * 2);
+              w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            } else {
+              const u32x2 v = *reinterpret_cast<const u32x2*>(sq[j] + st * 2);
+              w[0] = v.x; w[1] = v.y; w[2] = 0u; w[3] = 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) bv[u][j].s = (w[u / 2] >> ((u % 2) * 16 + sh)) & 0xFFu;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int j = 0; j < NS; ++j) bv[u][j] = load_b(j, st + u);
+        }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
