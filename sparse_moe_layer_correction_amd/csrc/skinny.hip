@@ -48,9 +48,19 @@ __device__ __forceinline__ u32x4 mx_decode8(u32x2 c, uint32_t s) {
 #endif
 // Grouped MX products with wide outputs take 4 slabs per wave (one set of
 // activation fragments serves 4 weight fragments) when that still leaves this
-// many waves: measured faster for the expert up product of a 64-token decode
-// (N = 5120), no better for N = 2048, and slower with bf16 weights.
-constexpr int64_t kGroupedWideWaves = 4096;
+// many waves. Measured on a 64-token decode: faster for the expert up product
+// (N = 5120) in both formats, for N = 2048 faster with MXFP4 (0.92 -> 0.70 ms)
+// and slower with MXFP8 (1.03 -> 1.19 ms); slower with bf16 weights.
+#ifndef MOE_SKINNY_WIDE_WAVES
+#define MOE_SKINNY_WIDE_WAVES 4096
+#endif
+#ifndef MOE_SKINNY_WIDE_MIN_N
+#define MOE_SKINNY_WIDE_MIN_N 4096       // MXFP8
+#endif
+#ifndef MOE_SKINNY_WIDE_MIN_N4
+#define MOE_SKINNY_WIDE_MIN_N4 2048      // MXFP4
+#endif
+constexpr int64_t kGroupedWideWaves = MOE_SKINNY_WIDE_WAVES;
 
 // Four results rounded to bf16, each added to its bf16 residual in fp32 (exact)
 // and rounded once more: the block's residual add.
@@ -99,7 +109,9 @@ __device__ __forceinline__ u32x4 mx4_decode8(uint32_t c, uint32_t s) {
 
 int skinny_slabs_per_wave(const SkinnyProblem& P) {
   if (P.offsets == nullptr) return P.M > 16 ? 4 : 1;
-  const bool wide = P.mx_codes != nullptr && P.N >= 4096 && (int64_t)P.groups * ((P.N + 63) / 64) >= kGroupedWideWaves;
+  const int min_n = P.mx_fp4 ? MOE_SKINNY_WIDE_MIN_N4 : MOE_SKINNY_WIDE_MIN_N;
+  const bool wide =
+      P.mx_codes != nullptr && P.N >= min_n && (int64_t)P.groups * ((P.N + 63) / 64) >= kGroupedWideWaves;
   return wide ? 4 : 1;
 }
 
