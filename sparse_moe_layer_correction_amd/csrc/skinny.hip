@@ -331,6 +331,101 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
   }
 }
 
+// MXFP4 experts in 128-deep k pairs (K a multiple of 128, one K segment, 16
+// rows). Lane group g = lane / 16 holds k = 32g .. 32g+31 of a pair, so its
+// codes are one 16-byte load and the four lane groups of a row read 64
+// consecutive bytes: with 64-deep steps a lane's 8 bytes left each row's cache
+// line request serving 32 bytes, and the kernel was bound by those requests.
+// The lane's k are one scale block (block g of the pair's four), and MFMA q of
+// the pair takes its k 32g + 8q .. +7 of the codes and, in the same order, of
+// the activations, so the products are unchanged. The scales of UNROLL pairs
+// are a row's 4 * UNROLL consecutive bytes, read in one load.
+template <int NS, int UNROLL>
+__device__ __forceinline__ void skinny_tile_mx4(const SkinnyProblem& P, int n_first, int rows, int row0,
+                                                const int32_t* gather, int64_t b_base, int out_row0, int lane,
+                                                int epi) {
+  static_assert(UNROLL == 4, "scale block of four pairs");
+  const KSeg& S = P.seg[0];
+  const int g = lane >> 4;
+  const int m = min(lane & 15, rows - 1);
+  const int64_t arow = gather ? (int64_t)gather[row0 + m] : (int64_t)(row0 + m);
+  const uint16_t* ap = S.A + arow * S.lda + 32 * g;
+  const uint8_t* cp[NS];
+  const uint8_t* sq[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int nr = min(n_first + j * 16 + (lane & 15), P.Nb - 1);
+    cp[j] = P.mx_codes + (b_base + (int64_t)nr * S.ldb + 32 * g) / 2;
+    sq[j] = P.mx_scales + b_base / 32 + (int64_t)nr * (S.ldb / 32);
+  }
+  f32x4v acc[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) acc[j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  const bool sblock = (S.ldb / 32) % (4 * UNROLL) == 0 && (b_base / 32) % (4 * UNROLL) == 0 &&
+                      (reinterpret_cast<uintptr_t>(P.mx_scales) & (4 * UNROLL - 1)) == 0;
+  auto pair = [&](const u32x4 (&c)[NS], const uint32_t (&sc)[NS], const u32x4 (&a)[4]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mx4_decode8(c[j][q], sc[j])),
+                                                         __builtin_bit_cast(bf16x8, a[q]), acc[j], 0, 0, 0);
+  };
+  const int npairs = S.K / 128;
+  int p = 0;
+  for (; p + UNROLL <= npairs; p += UNROLL) {
+    u32x4 c[UNROLL][NS], a[UNROLL][4];
+    uint32_t sc[UNROLL][NS];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) c[u][j] = *reinterpret_cast<const u32x4*>(cp[j] + (p + u) * 64);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (sblock) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(sq[j] + 4 * p);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) sc[u][j] = (w[u] >> (8 * g)) & 0xFFu;
+      } else {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) sc[u][j] = sq[j][4 * (p + u) + g];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[u][q] = *reinterpret_cast<const u32x4*>(ap + (p + u) * 128 + 8 * q);
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) pair(c[u], sc[u], a[u]);
+  }
+  for (; p < npairs; ++p) {
+    u32x4 c[NS], a[4];
+    uint32_t sc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      c[j] = *reinterpret_cast<const u32x4*>(cp[j] + p * 64);
+      sc[j] = sq[j][4 * p + g];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = *reinterpret_cast<const u32x4*>(ap + p * 128 + 8 * q);
+    pair(c, sc, a);
+  }
+  // lane l holds row l % 16 and columns 4 * (l / 16) + 0..3 of each slab
+  const int mr = lane & 15;
+  if (mr >= rows) return;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int n = n_first + j * 16 + (lane >> 4) * 4;
+    if (n >= P.N) continue;
+    f32x4v v = acc[j];
+    if (epi == EPI_RELU2_BF16) {
+      v[0] = relu2(v[0]); v[1] = relu2(v[1]); v[2] = relu2(v[2]); v[3] = relu2(v[3]);
+    }
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)(out_row0 + mr) * P.ldc + n) =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+}
+
 // One wavefront per (group, column block, k split); 4 waves per workgroup. A
 // column block is NSB slabs of 16 columns.
 // GROUPED_EPI: -1 for dense products (epilogue from the problem), else the
@@ -380,6 +475,13 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
     // MX experts: passes of 16 rows (an expert of a decode batch has a few;
     // more rows read its weights again). Keeping only the one-tile variant
     // leaves room for twice the codes in flight per lane at the same occupancy.
+    if constexpr (BMODE == kSkinnyMx4) {
+      if (GROUPED_EPI >= 0 && P.partial == nullptr && P.residual == nullptr && P.seg[0].K % 128 == 0) {
+        for (int r0 = 0; r0 < rows; r0 += 16)
+          skinny_tile_mx4<NSB, 4>(P, n_first, min(16, rows - r0), row0 + r0, P.gather, b_base, row0 + r0, lane, epi);
+        return;
+      }
+    }
     for (int r0 = 0; r0 < rows; r0 += 16)
       skinny_tile<1, NSB, unroll_steps(1, NSB, BMODE), BMODE>(P, n_first, min(16, rows - r0), row0 + r0, P.gather,
                                                              b_base, k_begin, k_end, row0 + r0, partial, lane, epi);
