@@ -207,16 +207,19 @@ gemm_bf16_kernel(const GemmLaunch L) {
   }
 
   // In the grouped products (the instantiations with a fixed epilogue), an
-  // expert's tail tile with at most BM/2 valid rows runs the half path: the same
-  // waves split BM/2 rows, so it costs about half a full tile instead of a full
-  // one (the tail tiles are about a sixth of the padded rows at 704 rows per
-  // expert).
-  constexpr bool kHalfTiles = BM == 256 && WM == 2 && EPI >= 0;
+  // expert's tail tile with at most BM/2 or 3*BM/4 valid rows runs a shorter
+  // tile: the same waves split BM/2 or 3*BM/4 rows, so it costs about half or
+  // three quarters of a full tile instead of a full one (the tail tiles are
+  // about a sixth of the padded rows at 704 rows per expert). Mode q runs q
+  // quarters of the tile's rows.
+  constexpr bool kShortTiles = BM == 256 && WM == 2 && EPI >= 0;
   auto body = [&](const GemmProblem& P, auto mode) __attribute__((always_inline)) {
-    constexpr bool HALF = decltype(mode)::value == 1;
-    constexpr int NAX = HALF ? NA / 2 : NA;        // A loads per thread per k tile
-    constexpr int TMX = HALF ? TM / 2 : TM;        // 32-row MFMA tiles per wave
-    constexpr int WTMX = HALF ? WTM / 2 : WTM;     // wave tile rows
+    constexpr int Q = decltype(mode)::value;       // quarters of BM
+    static_assert(Q == 2 || Q == 3 || Q == 4, "tile height");
+    constexpr int NAX = NA * Q / 4;                // A loads per thread per k tile
+    constexpr int TMX = TM * Q / 4;                // 32-row MFMA tiles per wave
+    constexpr int WTMX = WTM * Q / 4;              // wave tile rows
+    static_assert(Q == 4 || (NA * Q % 4 == 0 && TM * Q % 4 == 0), "short tile shape");
     // Load i of a thread fills LDS chunks [(wave*NAX + i)*64, +64) of the A stage
     // (64 lanes x 16 bytes, contiguous), lane l taking chunk position p: row
     // p / 8, slot p % 8, which holds logical chunk swz_slot(row, slot). Rows are
@@ -486,13 +489,17 @@ gemm_bf16_kernel(const GemmLaunch L) {
       else *reinterpret_cast<u32x2*>(dst) = u32x2{o[0], o[1]};
     }
   };
-  if constexpr (kHalfTiles) {
+  if constexpr (kShortTiles) {
     if (mend - m0 <= BM / 2) {
-      body(L.p[0], Stage<1>{});
+      body(L.p[0], Stage<2>{});
+      return;
+    }
+    if (mend - m0 <= 3 * BM / 4) {
+      body(L.p[0], Stage<3>{});
       return;
     }
   }
-  body(L.p[pi], Stage<0>{});
+  body(L.p[pi], Stage<4>{});
 }
 
 }  // namespace moe

@@ -220,12 +220,23 @@ def _compare_tokens(d, out, ws, lay, tokens, idx_gpu, label):
                                        ("tiny", dict(T=333, H=320, L=192, E=24, I=448, Is=576, K=5)),
                                        ("tiny", dict(T=29, H=320, L=192, E=24, I=448, Is=576, K=5)),
                                        # one expert: every token's one slot goes to it
-                                       ("tiny", dict(T=300, E=1, K=1)), ("tiny", dict(T=7, E=1, K=1))])
+                                       ("tiny", dict(T=300, E=1, K=1)), ("tiny", dict(T=7, E=1, K=1)),
+                                       # about 175 / 287 rows per expert: expert tails of 129-192
+                                       # rows (three-quarter-height tiles) / full plus short tails
+                                       ("tiny", dict(T=700, E=4, K=1)), ("tiny", dict(T=1150, E=4, K=1))])
 def test_forward_tiny_full(name, over):
     d = device_inputs(name, **over)
     cfg = d["cfg"]
     out, ws, lay = run_forward(d)
     idx = ws_view(ws, lay, "idx", torch.int32, (cfg.T, cfg.K)).cpu().numpy()
+    if cfg.T * cfg.K > 64:
+        # the 256-row expert tiles' tail heights this case covers (half: <= 128 rows,
+        # three quarters: <= 192, full)
+        counts = np.diff(ws_view(ws, lay, "offsets", torch.int32, (cfg.E + 1,)).cpu().numpy())
+        tails = [int(c - 256 * ((c - 1) // 256)) for c in counts if c > 0]
+        log(f"[tiles] expert rows {counts.tolist()} tails {tails}")
+        if over.get("T") == 700 and over.get("E") == 4:
+            assert any(128 < t <= 192 for t in tails)
     tokens = np.arange(cfg.T)
     _compare_tokens(d, out, ws, lay, tokens, idx, f"{name}{over}")
     # the expert intermediates too, row by row in the permuted order
