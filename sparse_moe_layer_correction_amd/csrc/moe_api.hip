@@ -23,7 +23,13 @@ constexpr int kGroupedBM = 256;
 // (few-row) kernels instead of the tiled MFMA GEMM.
 constexpr int kSkinnyMaxT = 64;
 // Dense skinny products split K until about this many waves are in flight.
-constexpr int kSkinnyTargetWaves = 2048;
+#ifndef MOE_SKINNY_TARGET_WAVES
+#define MOE_SKINNY_TARGET_WAVES 2048
+#endif
+#ifndef MOE_SKINNY_KSPLIT_DIV
+#define MOE_SKINNY_KSPLIT_DIV 4
+#endif
+constexpr int kSkinnyTargetWaves = MOE_SKINNY_TARGET_WAVES;
 
 int skinny_ksplit(int N, int K, int M) {
   if (N <= 0 || K < 64) return 1;
@@ -31,8 +37,10 @@ int skinny_ksplit(int N, int K, int M) {
   const int slabs = (N + width - 1) / width;
   int ks = (kSkinnyTargetWaves + slabs - 1) / slabs;
   // the fp32 partials are written once and read once: 8*ks*M*N bytes against
-  // 2*N*K bytes of weights; keep them within a quarter of the weight traffic
-  const int cap = std::max(1, K / (16 * std::max(M, 1)));
+  // 2*N*K bytes of weights; keep them within the weight traffic (a quarter of
+  // it left a 64-token decode's dense products with 64-256 waves: measured
+  // 12-42 % slower per product)
+  const int cap = std::max(1, K / (MOE_SKINNY_KSPLIT_DIV * std::max(M, 1)));
   ks = std::max(1, std::min(std::min(ks, cap), K / 64));   // whole 64-deep steps per split
   return ks;
 }
