@@ -48,10 +48,10 @@ struct GemmProblem {
   int N;                     // columns of C that are stored (multiple of 4)
   int Nb;                    // valid B rows (columns >= Nb reuse row Nb-1, results unused)
   const int32_t* gather;     // nullable: A row of output row r is gather[r]
-  const int32_t* tile_e;     // nullable: grouped mode tile table (expert of M tile);
+  const int32_t* tile_info;  // nullable: grouped mode M-tile table, 4 ints per M tile: its
+                             //   expert e, e's first M tile, offsets[e], offsets[e+1];
                              //   a grouped launch holds exactly one problem
   const int32_t* n_mtiles;   //   device scalar: number of valid M tiles
-  const int32_t* first_mtile;  // [E] each expert's first M tile in the table
   const int32_t* offsets;    //   [E+1] expert row offsets
   int64_t b_estride;         //   elements between consecutive experts' B
   void* C;
@@ -172,7 +172,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
 
   int pi = 0, m0, mend, n0;
   int64_t b_base = 0;
-  if (L.p[0].tile_e != nullptr) {
+  if (L.p[0].tile_info != nullptr) {
     // grouped: the grid is sized for the most M tiles any routing can need; only
     // the first n_mtiles * ntiles workgroups work, and the XCD renumbering runs
     // over exactly those, so every XCD gets an equal share
@@ -183,13 +183,13 @@ gemm_bf16_kernel(const GemmLaunch L) {
     // expert by expert: the tiles of one expert are contiguous in the order,
     // M fastest, so the M tiles that share a weight panel run side by side
     // (an expert's ne M tiles times ntl N tiles are contiguous in t, starting at
-    // first_mtile[e] * ntl, so t / ntl lands on one of the expert's own M tiles;
-    // its tiles start at its first permuted row, offsets[e], BM rows apart).
-    // Every table read here is one dependent step of the workgroup's start.
+    // its first M tile f times ntl, so t / ntl lands on one of the expert's own
+    // M tiles, whose entry holds e, f and the expert's rows; its tiles start at
+    // its first permuted row, offsets[e], BM rows apart). Every table read here
+    // is one dependent step of the workgroup's start, so the entry is one read.
     const int t = xcd_remap(blockIdx.x, valid);
-    const int e = L.p[0].tile_e[t / ntl];
-    const int f = L.p[0].first_mtile[e];
-    const int o0 = L.p[0].offsets[e], o1 = L.p[0].offsets[e + 1];
+    const int4 info = reinterpret_cast<const int4*>(L.p[0].tile_info)[t / ntl];
+    const int e = info.x, f = info.y, o0 = info.z, o1 = info.w;
     const int ne = (o1 - o0 + BM - 1) / BM;
     const int local = t - f * ntl;
     m0 = o0 + (local % ne) * BM;

@@ -64,11 +64,10 @@ struct PermuteScratch {
   uint64_t* masks;     // [E][nblk]
   int32_t* base;       // [E][nblk]
   int32_t* counts;     // [E]
-  int32_t* tile_e;     // [max_mtiles]
+  int32_t* tile_info;  // [max_mtiles][4]: each M tile's expert e, its first M tile, offsets[e], offsets[e+1]
   int32_t* n_mtiles;   // [1]
   int32_t* touched;    // [E] experts with at least one token, ascending
   int32_t* n_touched;  // [1]
-  int32_t* first_mtile;  // [E] index of each expert's first M tile in the tile table
 };
 
 hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* parts, hipStream_t st);

@@ -49,7 +49,7 @@ struct Layout {
   // route
   size_t wsplit, logits;
   // permute
-  size_t masks, base, counts, tile_e, n_mtiles, touched, n_touched, first_mtile;
+  size_t masks, base, counts, tile_info, n_mtiles, touched, n_touched;
   // forward
   size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial;
   size_t route_end, permute_begin, permute_end, total;
@@ -113,11 +113,10 @@ Layout make_layout(const moe_dims& d) {
   l.masks = take(E * l.nblk * 8);
   l.base = take(E * l.nblk * 4);
   l.counts = take(E * 4);
-  l.tile_e = take((size_t)l.max_mtiles * 4);
+  l.tile_info = take((size_t)l.max_mtiles * 16);
   l.n_mtiles = take(4);
   l.touched = take(E * 4);
   l.n_touched = take(4);
-  l.first_mtile = take(E * 4);
   l.permute_end = o;
   l.idx = take(TK * 4);
   l.gate = take(TK * 4);
@@ -267,10 +266,9 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
 // The permute scratch of a workspace whose first byte sits at layout offset `origin`.
 PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
   return PermuteScratch{at<uint64_t>(ws, l.masks - origin), at<int32_t>(ws, l.base - origin),
-                        at<int32_t>(ws, l.counts - origin),   at<int32_t>(ws, l.tile_e - origin),
+                        at<int32_t>(ws, l.counts - origin),   at<int32_t>(ws, l.tile_info - origin),
                         at<int32_t>(ws, l.n_mtiles - origin),
-                        at<int32_t>(ws, l.touched - origin),  at<int32_t>(ws, l.n_touched - origin),
-                        at<int32_t>(ws, l.first_mtile - origin)};
+                        at<int32_t>(ws, l.touched - origin),  at<int32_t>(ws, l.n_touched - origin)};
 }
 
 }  // namespace
@@ -480,9 +478,8 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.N = d.I;
     p.Nb = d.I;
     p.gather = row_token;
-    p.tile_e = ps.tile_e;
+    p.tile_info = ps.tile_info;
     p.n_mtiles = ps.n_mtiles;
-    p.first_mtile = ps.first_mtile;
     p.offsets = offsets;
     p.b_estride = I * L;
     p.C = h;
@@ -510,9 +507,8 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     GemmProblem& p = G.p[0];
     p.N = d.L;
     p.Nb = d.L;
-    p.tile_e = ps.tile_e;
+    p.tile_info = ps.tile_info;
     p.n_mtiles = ps.n_mtiles;
-    p.first_mtile = ps.first_mtile;
     p.offsets = offsets;
     p.b_estride = L * I;
     p.C = y;

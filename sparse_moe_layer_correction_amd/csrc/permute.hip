@@ -55,9 +55,9 @@ __global__ void __launch_bounds__(256) expert_scan_kernel(const uint64_t* __rest
 // the experts that received at least one token, in ascending order. Returns
 // the exclusive offset of expert tid.
 __device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __restrict__ offsets,
-                                              int32_t* __restrict__ tile_e,
+                                              int32_t* __restrict__ tile_info,
                                               int32_t* __restrict__ n_mtiles, int32_t* __restrict__ touched,
-                                              int32_t* __restrict__ n_touched, int32_t* __restrict__ first_mtile) {
+                                              int32_t* __restrict__ n_touched) {
   __shared__ int wsum_c[16], wsum_t[16], wsum_h[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nt = (c + BM - 1) / BM;
@@ -72,8 +72,8 @@ __device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __r
   const int ex_c = pc + ic - c, ex_t = pt + it - nt, ex_h = ph + ih - hit;
   if (tid < E) {
     offsets[tid] = ex_c;
-    first_mtile[tid] = ex_t;
-    for (int i = 0; i < nt; ++i) tile_e[ex_t + i] = tid;
+    for (int i = 0; i < nt; ++i)
+      reinterpret_cast<int4*>(tile_info)[ex_t + i] = make_int4(tid, ex_t, ex_c, ex_c + c);
     if (hit) touched[ex_h] = tid;
   }
   if (tid == E - 1) {
@@ -86,13 +86,12 @@ __device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __r
 
 __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict__ counts, int E, int BM,
                                                        int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ tile_e,
+                                                       int32_t* __restrict__ tile_info,
                                                        int32_t* __restrict__ n_mtiles,
                                                        int32_t* __restrict__ touched,
-                                                       int32_t* __restrict__ n_touched,
-                                                       int32_t* __restrict__ first_mtile) {
+                                                       int32_t* __restrict__ n_touched) {
   const int c = (int)threadIdx.x < E ? counts[threadIdx.x] : 0;
-  layout_experts(c, E, BM, offsets, tile_e, n_mtiles, touched, n_touched, first_mtile);
+  layout_experts(c, E, BM, offsets, tile_info, n_mtiles, touched, n_touched);
 }
 
 // All of steps 1-4 in one workgroup when the tokens fit one 64-token block
@@ -100,11 +99,10 @@ __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict
 // one launch instead of four.
 __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx, int T, int K, int E,
                                                              int BM, int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ tile_e,
+                                                             int32_t* __restrict__ tile_info,
                                                              int32_t* __restrict__ n_mtiles,
                                                              int32_t* __restrict__ touched,
                                                              int32_t* __restrict__ n_touched,
-                                                             int32_t* __restrict__ first_mtile,
                                                              int32_t* __restrict__ row_token,
                                                              int32_t* __restrict__ slot_row) {
   __shared__ unsigned long long m[kMaxExperts];
@@ -119,7 +117,7 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
   }
   __syncthreads();
   const int c = tid < E ? __popcll(m[tid]) : 0;
-  const int ex = layout_experts(c, E, BM, offsets, tile_e, n_mtiles, touched, n_touched, first_mtile);
+  const int ex = layout_experts(c, E, BM, offsets, tile_info, n_mtiles, touched, n_touched);
   if (tid < E) off[tid] = ex;
   __syncthreads();
   for (int s = tid; s < tk; s += blockDim.x) {
@@ -171,14 +169,14 @@ hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, 
                                int32_t* offsets, int32_t* row_token, int32_t* slot_row, hipStream_t st) {
   const int nblk = (T + 63) / 64;
   if (nblk == 1) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, T, K, E, BM, offsets, ps.tile_e,
-                       ps.n_mtiles, ps.touched, ps.n_touched, ps.first_mtile, row_token, slot_row);
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, T, K, E, BM, offsets, ps.tile_info,
+                       ps.n_mtiles, ps.touched, ps.n_touched, row_token, slot_row);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(block_masks_kernel, dim3(nblk), dim3(256), 0, st, idx, T, K, E, nblk, ps.masks);
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, st, ps.masks, nblk, E, ps.base, ps.counts);
-  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, ps.counts, E, BM, offsets, ps.tile_e,
-                     ps.n_mtiles, ps.touched, ps.n_touched, ps.first_mtile);
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, ps.counts, E, BM, offsets, ps.tile_info,
+                     ps.n_mtiles, ps.touched, ps.n_touched);
   const int64_t tk = (int64_t)T * K;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st, idx, T, K, E, nblk,
                      ps.masks, ps.base, offsets, row_token, slot_row);
