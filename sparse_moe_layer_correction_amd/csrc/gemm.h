@@ -68,6 +68,8 @@ struct GemmLaunch {
   GemmProblem p[2];
   int np;
   int tiles0;                // tiles of problem 0 (mtiles * ntiles)
+  int* counters;             // grouped launches: nullable, 8 zeroed ints (one per XCD) that hand
+                             //   out the tiles; without them workgroup b takes a fixed tile
 };
 
 // Workgroup i runs on XCD i % 8. Renumber so that each XCD walks a contiguous
@@ -173,13 +175,47 @@ gemm_bf16_kernel(const GemmLaunch L) {
   int pi = 0, m0, mend, n0;
   int64_t b_base = 0;
   if (L.p[0].tile_info != nullptr) {
-    // grouped: the grid is sized for the most M tiles any routing can need; only
-    // the first n_mtiles * ntiles workgroups work, and the XCD renumbering runs
-    // over exactly those, so every XCD gets an equal share
-    const int mtv = *L.p[0].n_mtiles;
+    // grouped: the grid is sized for the most M tiles any routing can need, and
+    // n_mtiles * ntiles of those workgroups get a tile; the tiles are split over
+    // the XCDs in equal contiguous ranges (see xcd_remap)
     const int ntl = L.p[0].ntiles;
-    const int valid = mtv * ntl;
-    if ((int)blockIdx.x >= valid) return;
+    int t;
+    if (L.counters != nullptr) {
+      // Each XCD's tiles are handed out in order by its counter, to the
+      // workgroups that run on it; one whose XCD is done takes a tile still
+      // left to another XCD. XCDs run the grouped products a few per cent
+      // apart, and with fixed tiles the slowest one ended the launch alone.
+      __shared__ int claim;
+      if (tid == 0) {
+        const int x = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // XCC_ID
+        const int v = atomicAdd(&L.counters[x], 1);
+        const int valid = *L.p[0].n_mtiles * ntl;
+        const int q = valid / 8, r = valid % 8;
+        int tt = -1;
+        if (v < q + (x < r ? 1 : 0)) {
+          tt = x * q + min(x, r) + v;
+        } else {
+          int seen[8];
+#pragma unroll
+          for (int y = 0; y < 8; ++y) seen[y] = __hip_atomic_load(&L.counters[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int d = 1; d < 8 && tt < 0; ++d) {
+            const int y = (x + d) & 7;
+            const int sz = q + (y < r ? 1 : 0);
+            if (seen[y] >= sz) continue;
+            const int w = atomicAdd(&L.counters[y], 1);
+            if (w < sz) tt = y * q + min(y, r) + w;
+          }
+        }
+        claim = tt;
+      }
+      __syncthreads();
+      t = __builtin_amdgcn_readfirstlane(claim);
+      if (t < 0) return;
+    } else {
+      const int valid = *L.p[0].n_mtiles * ntl;
+      if ((int)blockIdx.x >= valid) return;
+      t = xcd_remap(blockIdx.x, valid);
+    }
     // expert by expert: the tiles of one expert are contiguous in the order,
     // M fastest, so the M tiles that share a weight panel run side by side
     // (an expert's ne M tiles times ntl N tiles are contiguous in t, starting at
@@ -187,7 +223,6 @@ gemm_bf16_kernel(const GemmLaunch L) {
     // M tiles, whose entry holds e, f and the expert's rows; its tiles start at
     // its first permuted row, offsets[e], BM rows apart). Every table read here
     // is one dependent step of the workgroup's start, so the entry is one read.
-    const int t = xcd_remap(blockIdx.x, valid);
     const int4 info = reinterpret_cast<const int4*>(L.p[0].tile_info)[t / ntl];
     const int e = info.x, f = info.y, o0 = info.z, o1 = info.w;
     const int ne = (o1 - o0 + BM - 1) / BM;

@@ -9,6 +9,8 @@
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
+// tile counters of the forward's expert-down GEMM launch (one per XCD)
+constexpr int kGemmCounters = 8;
 constexpr int kMaxTopK = 64;
 constexpr int kMaxGroups = 64;      // one group per lane of the top-K wave
 
@@ -68,6 +70,7 @@ struct PermuteScratch {
   int32_t* n_mtiles;   // [1]
   int32_t* touched;    // [E] experts with at least one token, ascending
   int32_t* n_touched;  // [1]
+  int32_t* gemm_ctr;   // [kGemmCounters] zeroed here for the grouped GEMMs that follow
 };
 
 hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* parts, hipStream_t st);

@@ -49,7 +49,7 @@ struct Layout {
   // route
   size_t wsplit, logits;
   // permute
-  size_t masks, base, counts, tile_info, n_mtiles, touched, n_touched;
+  size_t masks, base, counts, tile_info, n_mtiles, touched, n_touched, gemm_ctr;
   // forward
   size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial;
   size_t route_end, permute_begin, permute_end, total;
@@ -117,6 +117,7 @@ Layout make_layout(const moe_dims& d) {
   l.n_mtiles = take(4);
   l.touched = take(E * 4);
   l.n_touched = take(4);
+  l.gemm_ctr = take(kGemmCounters * 4);
   l.permute_end = o;
   l.idx = take(TK * 4);
   l.gate = take(TK * 4);
@@ -268,7 +269,8 @@ PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
   return PermuteScratch{at<uint64_t>(ws, l.masks - origin), at<int32_t>(ws, l.base - origin),
                         at<int32_t>(ws, l.counts - origin),   at<int32_t>(ws, l.tile_info - origin),
                         at<int32_t>(ws, l.n_mtiles - origin),
-                        at<int32_t>(ws, l.touched - origin),  at<int32_t>(ws, l.n_touched - origin)};
+                        at<int32_t>(ws, l.touched - origin),  at<int32_t>(ws, l.n_touched - origin),
+                        at<int32_t>(ws, l.gemm_ctr - origin)};
 }
 
 }  // namespace
@@ -518,6 +520,12 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.ntiles = (d.L + ts.BN - 1) / ts.BN;
     p.group_m = 4;
     add_seg(p, h, I, w->w_down, I, d.I);
+    // tiles handed out by per-XCD counters (zeroed by the permutation above):
+    // the claim adds about a microsecond to a tile's start, which the 80-k-tile
+    // down product's tiles repay by balancing the XCDs (Ultra prefill, two
+    // boxes: 7.25 -> 7.09 and 7.13 -> 7.06 ms) and the up product's
+    // 32-k-tile ones do not (7.54 -> 7.67 ms)
+    G.counters = ps.gemm_ctr;
     if (mk.mark(MOE_PHASE_EXPERT_DOWN) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm(G, kGroupedCfg, stream) != hipSuccess) return MOE_ERR_HIP;
   }

@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(256) expert_scan_kernel(const uint64_t* __rest
 __device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __restrict__ offsets,
                                               int32_t* __restrict__ tile_info,
                                               int32_t* __restrict__ n_mtiles, int32_t* __restrict__ touched,
-                                              int32_t* __restrict__ n_touched) {
+                                              int32_t* __restrict__ n_touched, int32_t* __restrict__ gemm_ctr) {
   __shared__ int wsum_c[16], wsum_t[16], wsum_h[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nt = (c + BM - 1) / BM;
@@ -70,6 +70,7 @@ __device__ __forceinline__ int layout_experts(int c, int E, int BM, int32_t* __r
   int pc = 0, pt = 0, ph = 0;
   for (int w = 0; w < wave; ++w) { pc += wsum_c[w]; pt += wsum_t[w]; ph += wsum_h[w]; }
   const int ex_c = pc + ic - c, ex_t = pt + it - nt, ex_h = ph + ih - hit;
+  if (tid < kGemmCounters) gemm_ctr[tid] = 0;
   if (tid < E) {
     offsets[tid] = ex_c;
     for (int i = 0; i < nt; ++i)
@@ -89,9 +90,10 @@ __global__ void __launch_bounds__(1024) offsets_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ tile_info,
                                                        int32_t* __restrict__ n_mtiles,
                                                        int32_t* __restrict__ touched,
-                                                       int32_t* __restrict__ n_touched) {
+                                                       int32_t* __restrict__ n_touched,
+                                                       int32_t* __restrict__ gemm_ctr) {
   const int c = (int)threadIdx.x < E ? counts[threadIdx.x] : 0;
-  layout_experts(c, E, BM, offsets, tile_info, n_mtiles, touched, n_touched);
+  layout_experts(c, E, BM, offsets, tile_info, n_mtiles, touched, n_touched, gemm_ctr);
 }
 
 // All of steps 1-4 in one workgroup when the tokens fit one 64-token block
@@ -103,6 +105,7 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
                                                              int32_t* __restrict__ n_mtiles,
                                                              int32_t* __restrict__ touched,
                                                              int32_t* __restrict__ n_touched,
+                                                             int32_t* __restrict__ gemm_ctr,
                                                              int32_t* __restrict__ row_token,
                                                              int32_t* __restrict__ slot_row) {
   __shared__ unsigned long long m[kMaxExperts];
@@ -117,7 +120,7 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
   }
   __syncthreads();
   const int c = tid < E ? __popcll(m[tid]) : 0;
-  const int ex = layout_experts(c, E, BM, offsets, tile_info, n_mtiles, touched, n_touched);
+  const int ex = layout_experts(c, E, BM, offsets, tile_info, n_mtiles, touched, n_touched, gemm_ctr);
   if (tid < E) off[tid] = ex;
   __syncthreads();
   for (int s = tid; s < tk; s += blockDim.x) {
@@ -170,13 +173,13 @@ hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, 
   const int nblk = (T + 63) / 64;
   if (nblk == 1) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, T, K, E, BM, offsets, ps.tile_info,
-                       ps.n_mtiles, ps.touched, ps.n_touched, row_token, slot_row);
+                       ps.n_mtiles, ps.touched, ps.n_touched, ps.gemm_ctr, row_token, slot_row);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(block_masks_kernel, dim3(nblk), dim3(256), 0, st, idx, T, K, E, nblk, ps.masks);
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, st, ps.masks, nblk, E, ps.base, ps.counts);
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(1024), 0, st, ps.counts, E, BM, offsets, ps.tile_info,
-                     ps.n_mtiles, ps.touched, ps.n_touched);
+                     ps.n_mtiles, ps.touched, ps.n_touched, ps.gemm_ctr);
   const int64_t tk = (int64_t)T * K;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st, idx, T, K, E, nblk,
                      ps.masks, ps.base, offsets, row_token, slot_row);
