@@ -181,36 +181,36 @@ gemm_bf16_kernel(const GemmLaunch L) {
     const int ntl = L.p[0].ntiles;
     int t;
     if (L.counters != nullptr) {
-      // Each XCD's tiles are handed out in order by its counter, to the
-      // workgroups that run on it; one whose XCD is done takes a tile still
-      // left to another XCD. XCDs run the grouped products a few per cent
-      // apart, and with fixed tiles the slowest one ended the launch alone.
-      __shared__ int claim;
-      if (tid == 0) {
-        const int x = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // XCC_ID
-        const int v = atomicAdd(&L.counters[x], 1);
-        const int valid = *L.p[0].n_mtiles * ntl;
-        const int q = valid / 8, r = valid % 8;
-        int tt = -1;
-        if (v < q + (x < r ? 1 : 0)) {
-          tt = x * q + min(x, r) + v;
-        } else {
-          int seen[8];
-#pragma unroll
-          for (int y = 0; y < 8; ++y) seen[y] = __hip_atomic_load(&L.counters[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          for (int d = 1; d < 8 && tt < 0; ++d) {
+      // Each XCD's range is split into a fixed part, seven eighths of it, and a
+      // tail handed out in order by the XCD's counter: workgroup b (on XCD
+      // b % 8) takes fixed tile b / 8 while there is one, then claims from its
+      // XCD's tail and, once that is done, from another XCD's. XCDs run the
+      // grouped products a few per cent apart, and with fixed tiles the slowest
+      // one ended the launch alone; only the tail pays the claim's latency.
+      const int valid = *L.p[0].n_mtiles * ntl;
+      const int q = valid / 8, r = valid % 8;
+      const int x = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
+      const int size = q + (x < r ? 1 : 0), fixed = size - size / 8;
+      if (j < fixed) {
+        t = x * q + min(x, r) + j;
+      } else {
+        __shared__ int claim;
+        if (tid == 0) {
+          int tt = -1;
+          for (int d = 0; d < 8 && tt < 0; ++d) {
             const int y = (x + d) & 7;
-            const int sz = q + (y < r ? 1 : 0);
-            if (seen[y] >= sz) continue;
+            const int sy = q + (y < r ? 1 : 0), fy = sy - sy / 8;
+            if (d > 0 && __hip_atomic_load(&L.counters[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= sy - fy)
+              continue;                                  // that tail is done: no atomic
             const int w = atomicAdd(&L.counters[y], 1);
-            if (w < sz) tt = y * q + min(y, r) + w;
+            if (w < sy - fy) tt = y * q + min(y, r) + fy + w;
           }
+          claim = tt;
         }
-        claim = tt;
+        __syncthreads();
+        t = __builtin_amdgcn_readfirstlane(claim);
+        if (t < 0) return;
       }
-      __syncthreads();
-      t = __builtin_amdgcn_readfirstlane(claim);
-      if (t < 0) return;
     } else {
       const int valid = *L.p[0].n_mtiles * ntl;
       if ((int)blockIdx.x >= valid) return;

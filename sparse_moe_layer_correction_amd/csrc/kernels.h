@@ -9,8 +9,8 @@
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
-// tile counters of the forward's expert-down GEMM launch (one per XCD)
-constexpr int kGemmCounters = 8;
+// tile counters of the forward's grouped GEMM launches (8 per launch, one per XCD)
+constexpr int kGemmCounters = 16;
 constexpr int kMaxTopK = 64;
 constexpr int kMaxGroups = 64;      // one group per lane of the top-K wave
 

@@ -491,6 +491,7 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.ntiles = (d.I + ts.BN - 1) / ts.BN;
     p.group_m = 4;
     add_seg(p, z, L, w->w_up, L, d.L);
+    G.counters = ps.gemm_ctr;                  // the XCD tails' counters, zeroed by the permutation
     if (mk.mark(MOE_PHASE_EXPERT_UP) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm(G, kGroupedCfg, stream) != hipSuccess) return MOE_ERR_HIP;
   }
@@ -520,12 +521,7 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.ntiles = (d.L + ts.BN - 1) / ts.BN;
     p.group_m = 4;
     add_seg(p, h, I, w->w_down, I, d.I);
-    // tiles handed out by per-XCD counters (zeroed by the permutation above):
-    // the claim adds about a microsecond to a tile's start, which the 80-k-tile
-    // down product's tiles repay by balancing the XCDs (Ultra prefill, two
-    // boxes: 7.25 -> 7.09 and 7.13 -> 7.06 ms) and the up product's
-    // 32-k-tile ones do not (7.54 -> 7.67 ms)
-    G.counters = ps.gemm_ctr;
+    G.counters = ps.gemm_ctr + 8;              // the XCD tails' counters, zeroed by the permutation
     if (mk.mark(MOE_PHASE_EXPERT_DOWN) != hipSuccess) return MOE_ERR_HIP;
     if (launch_gemm(G, kGroupedCfg, stream) != hipSuccess) return MOE_ERR_HIP;
   }
