@@ -30,6 +30,8 @@ constexpr int kSkinnyMaxT = 64;
 #define MOE_SKINNY_KSPLIT_DIV 4
 #endif
 constexpr int kSkinnyTargetWaves = MOE_SKINNY_TARGET_WAVES;
+// tokens from which the tiled router product splits K in two
+constexpr int kRouterSplitMinT = 4096;
 
 int skinny_ksplit(int N, int K, int M) {
   if (N <= 0 || K < 64) return 1;
@@ -107,7 +109,7 @@ Layout make_layout(const moe_dims& d) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   l.wsplit = take(3 * E * H * 2);
-  l.logits = take(T * l.ldl * 4);
+  l.logits = take(2 * T * l.ldl * 4);           // two halves when the router product splits K
   l.route_end = o;
   l.permute_begin = o;
   l.masks = take(E * l.nblk * 8);
@@ -234,6 +236,7 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
               float* partial = nullptr) {
   uint16_t* parts = at<uint16_t>(ws, l.wsplit);
   float* logits = at<float>(ws, l.logits);
+  const float* logits2 = nullptr;
   const bool skinny = d.T <= kSkinnyMaxT && partial != nullptr;
   hipError_t e = hipSuccess;
   if (mk.mark(MOE_PHASE_ROUTER_SPLIT) != hipSuccess) return MOE_ERR_HIP;
@@ -249,6 +252,20 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
     add_seg(P, x, d.H, nullptr, d.H, d.H);
     P.f32_b = w_router;
     e = launch_skinny(P, st);
+  } else if (d.T >= kRouterSplitMinT && d.H % 128 == 0) {
+    // Many tokens: K split in two (each half of H over the three weight parts)
+    // so that 256x256 tiles fill the CUs (E = 512 columns make only 2 column
+    // tiles); the top-k adds the halves' fp32 logits. Ultra prefill: 0.43 ms
+    // with 128x128 tiles over the whole K.
+    const int Hh = d.H / 2;
+    GemmLaunch L{};
+    L.np = 2;
+    for (int h = 0; h < 2; ++h) {
+      L.p[h] = dense_problem(TILE_256x256, d.T, (int)l.ldl, d.E, logits + (int64_t)h * d.T * l.ldl, l.ldl, EPI_F32);
+      for (int s = 0; s < 3; ++s) add_seg(L.p[h], x + h * Hh, d.H, parts + s * EH + h * Hh, d.H, Hh);
+    }
+    e = launch_gemm(L, TILE_256x256, st);
+    logits2 = logits + (int64_t)d.T * l.ldl;
   } else {
     const int cfg = choose_dense_cfg(d.T, (int)l.ldl);
     GemmLaunch L{};
@@ -259,7 +276,7 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (mk.mark(MOE_PHASE_TOPK) != hipSuccess) return MOE_ERR_HIP;
-  e = launch_topk(logits, l.ldl, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d), topk_groups_of(d), idx, gate,
+  e = launch_topk(logits, logits2, l.ldl, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d), topk_groups_of(d), idx, gate,
                   gap, st);
   return hip_status(e);
 }

@@ -37,7 +37,8 @@ __global__ void split_router_weight_kernel(const float* __restrict__ w, int64_t 
 }
 
 template <int VPL>
-__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int64_t ldl,
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
+                                                   const float* __restrict__ logits2, int64_t ldl,
                                                    const float* __restrict__ bias, int T, int E, int K,
                                                    float scale, int n_group, int topk_group,
                                                    int32_t* __restrict__ idx, float* __restrict__ gate,
@@ -49,13 +50,14 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   float s[VPL];
   uint64_t key[VPL];
   const float* lrow = logits + (int64_t)t * ldl;
+  const float* lrow2 = logits2 ? logits2 + (int64_t)t * ldl : nullptr;   // the other half of a K split
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int e = j * 64 + lane;
     s[j] = 0.f;
     key[j] = 0;
     if (e < E) {
-      const float l = lrow[e];
+      const float l = lrow2 ? lrow[e] + lrow2[e] : lrow[e];
       const float sv = 1.0f / (1.0f + expf(-l));
       const float cv = sv + bias[e];
       s[j] = sv;
@@ -168,14 +170,14 @@ hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* pa
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int64_t ldl, const float* bias, int T, int E, int K,
+hipError_t launch_topk(const float* logits, const float* logits2, int64_t ldl, const float* bias, int T, int E, int K,
                        float scale, int n_group, int topk_group, int32_t* idx, float* gate, float* gap,
                        hipStream_t st) {
   const dim3 grid((T + 3) / 4), block(256);
   const int vpl = (E + 63) / 64;
 #define MOE_TOPK(V)                                                                                           \
-  hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, st, logits, ldl, bias, T, E, K, scale, n_group, topk_group, \
-                     idx, gate, gap)
+  hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, st, logits, logits2, ldl, bias, T, E, K, scale, n_group,   \
+                     topk_group, idx, gate, gap)
   if (vpl <= 1) MOE_TOPK(1);
   else if (vpl <= 2) MOE_TOPK(2);
   else if (vpl <= 4) MOE_TOPK(4);

@@ -61,6 +61,7 @@ def ws_view(ws, lay, name, dtype, shape):
     ("tiny", dict(K=16)),                    # K == E: every expert, gap = +inf
     ("tiny", dict(K=1)),
     ("nano", dict(T=1024)),
+    ("nano", dict(T=4096)),                  # from 4096 tokens the tiled router splits K in two
     ("super", dict(T=2048)),
     ("ultra_decode1", {}),
     ("ultra_decode64", {}),
