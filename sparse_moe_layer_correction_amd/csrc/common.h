@@ -64,25 +64,30 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 // max(v, the value DPP control CTRL brings from another lane), 0 (the identity
 // of an unsigned max) where the control brings nothing
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, ROW_MASK, 0xF, true);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, true);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = __builtin_amdgcn_update_dpp(0u, v, CTRL, ROW_MASK, 0xF, true);
   return o > v ? o : v;
 }
 
 // Max over the 64 lanes, returned to every lane. DPP moves (VALU latency) rather
 // than LDS permutes: row shifts by 1, 2, 4, 8 leave each 16-lane row's max in
 // its lane 15; broadcasts of lane 15 and lane 31 carry it to the last lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_max_u32<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_max_u32<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_max_u32<0x118, 0xF>(v);   // row_shr:8
+  v = dpp_max_u32<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max_u32<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// 64-bit max over the 64 lanes as two 32-bit ones: the high words', then the low
+// words' of the lanes that hold that high word (a 64-bit compare and two
+// selects per step cost the top-k's serial rounds about twice as much).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_u64<0x111, 0xF>(v);   // row_shr:1
-  v = dpp_max_u64<0x112, 0xF>(v);   // row_shr:2
-  v = dpp_max_u64<0x114, 0xF>(v);   // row_shr:4
-  v = dpp_max_u64<0x118, 0xF>(v);   // row_shr:8
-  v = dpp_max_u64<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-  v = dpp_max_u64<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
   return ((uint64_t)hi << 32) | lo;
 }
 
