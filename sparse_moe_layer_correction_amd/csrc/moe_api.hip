@@ -5,6 +5,8 @@
 
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -53,7 +55,7 @@ struct Layout {
   // permute
   size_t masks, base, counts, tile_info, n_mtiles, touched, n_touched, gemm_ctr;
   // forward
-  size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial;
+  size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial, partial2;
   size_t route_end, permute_begin, permute_end, total;
   int64_t ldl;         // logits row stride (E rounded up to 64)
   int nblk;            // token blocks of 64
@@ -141,6 +143,12 @@ Layout make_layout(const moe_dims& d) {
     p = std::max(p, (size_t)skinny_ksplit((int)Is, (int)H, (int)T) * T * Is * 4);
     p = std::max(p, (size_t)skinny_ksplit((int)H, (int)(L + Is), (int)T) * T * H * 4);
     take(p);
+    // fc1 and the shared up run on a second stream beside the router: partials of their own
+    l.partial2 = o;
+    take(std::max((size_t)skinny_ksplit((int)L, (int)H, (int)T) * T * L * 4,
+                  (size_t)skinny_ksplit((int)Is, (int)H, (int)T) * T * Is * 4));
+  } else {
+    l.partial2 = o;
   }
   l.total = o;
   return l;
@@ -397,6 +405,35 @@ size_t block_extra_bytes(const moe_dims& d) { return align_up((size_t)d.T * d.H 
 
 bool eps_ok(float eps) { return eps >= 0.f && eps <= 1e30f; }   // also rejects NaN
 
+// A second stream per device (default priority) and two events, created once:
+// a few-token forward runs fc1 and the shared expert's up product on it, beside
+// the router, top-k and permutation on the caller's stream (small,
+// latency-bound kernels), and joins it back before the expert products.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+const SideStream* side_stream() {
+  static std::mutex mu;
+  static SideStream per_dev[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  SideStream& ss = per_dev[dev];
+  if (ss.s == nullptr) {
+    SideStream n;
+    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      (void)hipStreamDestroy(n.s);
+      return nullptr;
+    }
+    ss = n;
+  }
+  return &ss;
+}
+
 int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
                  size_t ws_bytes, hipStream_t stream, const Marks& mk, const moe_experts_mx* mx = nullptr,
                  const BlockArgs* blk = nullptr) {
@@ -448,9 +485,43 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   uint16_t* y = at<uint16_t>(ws, l.y);
   uint16_t* y_lat = at<uint16_t>(ws, l.y_lat);
 
-  // 1. router
+  // 1. router; few tokens: fc1 and the shared up on the side stream meanwhile
+  // (the profiled forward keeps one stream, so that its phase marks bound
+  // its phases)
   const bool skinny = d.T <= kSkinnyMaxT;
   float* partial = skinny ? at<float>(ws, l.partial) : nullptr;
+  const SideStream* side = (skinny && mk.ev == nullptr) ? side_stream() : nullptr;
+  auto fc1_shared_up = [&](hipStream_t s, float* part) -> int {
+    SkinnyProblem P = skinny_dense(d.T, d.L, d.L, z, L, EPI_BF16, d.H, part);
+    add_seg(P, x, H, w->w_fc1, H, d.H);
+    if (launch_skinny(P, s) != hipSuccess) return MOE_ERR_HIP;
+    SkinnyProblem Q = skinny_dense(d.T, d.Is, d.Is, hs, Is, EPI_RELU2_BF16, d.H, part);
+    add_seg(Q, x, H, w->w_sh_up, H, d.H);
+    if (launch_skinny(Q, s) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+  };
+  // the caller's stream waits for the side stream's work on every way out,
+  // errors included (that work writes into the workspace)
+  struct Join {
+    const SideStream* side;
+    hipStream_t stream;
+    bool armed = false;
+    hipError_t now() {
+      armed = false;
+      return hipStreamWaitEvent(stream, side->join, 0);
+    }
+    ~Join() {
+      if (armed) (void)hipStreamWaitEvent(stream, side->join, 0);
+    }
+  } join{side, stream};
+  if (side != nullptr) {
+    if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      return MOE_ERR_HIP;
+    const int rs = fc1_shared_up(side->s, at<float>(ws, l.partial2));
+    if (hipEventRecord(side->join, side->s) != hipSuccess) return MOE_ERR_HIP;
+    join.armed = true;
+    if (rs != MOE_OK) return rs;
+  }
   int rc = run_route(d, l, x, w->w_router, w->corr_bias, idx, gate, at<float>(ws, l.gap), ws, stream, mk, partial);
   if (rc != MOE_OK) return rc;
 
@@ -463,12 +534,12 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   // 3. x read by one launch for fc1 (z) and the shared expert's up + relu^2 (hs)
   if (skinny) {
     if (mk.mark(MOE_PHASE_FC1_SHARED_UP) != hipSuccess) return MOE_ERR_HIP;
-    SkinnyProblem P = skinny_dense(d.T, d.L, d.L, z, L, EPI_BF16, d.H, partial);
-    add_seg(P, x, H, w->w_fc1, H, d.H);
-    if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
-    SkinnyProblem Q = skinny_dense(d.T, d.Is, d.Is, hs, Is, EPI_RELU2_BF16, d.H, partial);
-    add_seg(Q, x, H, w->w_sh_up, H, d.H);
-    if (launch_skinny(Q, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (side != nullptr) {
+      if (join.now() != hipSuccess) return MOE_ERR_HIP;
+    } else {
+      const int rs = fc1_shared_up(stream, partial);
+      if (rs != MOE_OK) return rs;
+    }
   } else {
     const int cfg = choose_dense_cfg(d.T, std::min(d.L, d.Is));
     GemmLaunch G{};
