@@ -224,7 +224,11 @@ def _compare_tokens(d, out, ws, lay, tokens, idx_gpu, label):
                                        ("tiny", dict(T=300, E=1, K=1)), ("tiny", dict(T=7, E=1, K=1)),
                                        # about 175 / 287 rows per expert: expert tails of 129-192
                                        # rows (three-quarter-height tiles) / full plus short tails
-                                       ("tiny", dict(T=700, E=4, K=1)), ("tiny", dict(T=1150, E=4, K=1))])
+                                       ("tiny", dict(T=700, E=4, K=1)), ("tiny", dict(T=1150, E=4, K=1)),
+                                       # 32 experts x about 256 rows x 4 column tiles: 128 grouped
+                                       # tiles, so each XCD's last eighth is claimed through its
+                                       # counter (every output and intermediate row checked)
+                                       ("tiny", dict(T=2048, H=512, L=256, E=32, I=1024, Is=512, K=4))])
 def test_forward_tiny_full(name, over):
     d = device_inputs(name, **over)
     cfg = d["cfg"]
