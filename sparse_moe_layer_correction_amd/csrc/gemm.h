@@ -180,7 +180,9 @@ gemm_bf16_kernel(const GemmLaunch L) {
     // the XCDs in equal contiguous ranges (see xcd_remap)
     const int ntl = L.p[0].ntiles;
     int t;
-    if (L.counters != nullptr) {
+    // (only the grouped instantiations, the fixed-epilogue ones, carry the
+    // claim: its LDS word would push the 64x256 tile past two workgroups per CU)
+    if (EPI >= 0 && L.counters != nullptr) {
       // Each XCD's range is split into a fixed part, seven eighths of it, and a
       // tail handed out in order by the XCD's counter: workgroup b (on XCD
       // b % 8) takes fixed tile b / 8 while there is one, then claims from its
