@@ -40,6 +40,9 @@ __device__ __forceinline__ u32x4 mx_decode8(u32x2 c, uint32_t s) {
 }
 
 // weight bytes each lane keeps in flight (the loop unroll follows from it)
+#ifndef MOE_SKINNY_DENSE64
+#define MOE_SKINNY_DENSE64 1
+#endif
 #ifndef MOE_SKINNY_INFLIGHT
 #define MOE_SKINNY_INFLIGHT 128
 #endif
@@ -426,6 +429,152 @@ __device__ __forceinline__ void skinny_tile_mx4(const SkinnyProblem& P, int n_fi
   }
 }
 
+// Dense products of 33..64 rows (a 64-token decode's fc1, shared up and fc2 +
+// shared down). With the rows in registers every wave reads all of them for
+// its k range: as many bytes of activations as of weights per step, each row a
+// cache-line request of its own, and the product ran at 1.7-2.6 TB/s. Here a
+// workgroup's four waves take 256 adjacent columns (4 slabs of 16 each) of one
+// k split, and a step's activations (64 rows x 64 k, 8 KB) are loaded once
+// into LDS (global -> LDS directly, two stages, the tiled GEMM's swizzle) and
+// read from there by the four waves; each wave streams its weights straight
+// into registers one step ahead, as the other skinny products do. One barrier
+// per step. Same k order and MFMA as skinny_tile (lane group g holds k 16g ..
+// 16g+15 of a step), so the products are the same.
+constexpr int kDense64Cols = 256;             // columns per workgroup
+__global__ void __launch_bounds__(256) skinny_dense64_kernel(const SkinnyProblem P) {
+  __shared__ u32x4 act[2][64 * 8];            // two stages of 64 rows x 8 chunks of 16 bytes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ngroups = (P.N + kDense64Cols - 1) / kDense64Cols;
+  const int ks = (int)blockIdx.x % P.ksplit, cg = (int)blockIdx.x / P.ksplit;
+  if (cg >= ngroups) return;
+  const int n_first = cg * kDense64Cols + wave * 64;
+  const bool active = n_first < P.N;          // a wave past the last column still loads and waits
+  const int M = P.M;
+  int ktot = 0;
+  for (int s = 0; s < P.nseg; ++s) ktot += P.seg[s].K;
+  const int ksteps = ktot / 64;
+  const int k_begin = (int)((int64_t)ksteps * ks / P.ksplit) * 64;
+  const int k_end = (int)((int64_t)ksteps * (ks + 1) / P.ksplit) * 64;
+  float* partial = P.partial ? P.partial + (int64_t)ks * P.M * P.N : nullptr;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  // this thread's two 16-byte chunks of a step's activations: LDS position p,
+  // row p / 8, slot p % 8 holding logical chunk swz_slot(row, slot) (rows past
+  // M repeat the last row; their results are not stored)
+  int drow[2], dchk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = (wave * 2 + i) * 64 + lane;
+    drow[i] = min(p / 8, M - 1);
+    dchk[i] = swz_slot(p / 8, p % 8);
+  }
+  f32x4v acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[j][t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+  int seg_k0 = 0;
+  for (int s = 0; s < P.nseg; ++s) {
+    const KSeg& S = P.seg[s];
+    const int lo = max(k_begin, seg_k0), hi = min(k_end, seg_k0 + S.K);
+    if (lo < hi) {                            // the same for the four waves
+      const int nsteps = (hi - lo) / 64;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(S.A);
+      uint32_t ao[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ao[i] = (uint32_t)((int64_t)drow[i] * S.lda * 2 + dchk[i] * 16);
+      auto dma = [&](int st, int stage) {
+        const int so = (lo - seg_k0 + st * 64) * 2;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)&act[stage][(wave * 2 + i) * 64], 16, (int)ao[i],
+                                                   so, 0, 0);
+      };
+      const uint16_t* bp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int nr = min(n_first + j * 16 + r16, P.Nb - 1);
+        bp[j] = S.B + (int64_t)nr * S.ldb + (lo - seg_k0) + 16 * g;
+      }
+      struct W {
+        u32x4 w0[4], w1[4];
+      };
+      auto wload = [&](int st) {
+        W r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r.w0[j] = *reinterpret_cast<const u32x4*>(bp[j] + st * 64);
+          r.w1[j] = *reinterpret_cast<const u32x4*>(bp[j] + st * 64 + 8);
+        }
+        return r;
+      };
+      W cur{}, nxt{};
+      dma(0, 0);
+      if (active) cur = wload(0);
+      MOE_WAIT_VMCNT(0);
+      __syncthreads();
+      for (int st = 0; st < nsteps; ++st) {
+        const int stg = st & 1;
+        if (st + 1 < nsteps) {
+          if (active) nxt = wload(st + 1);
+          dma(st + 1, stg ^ 1);
+        }
+        u32x4 a0[4], a1[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = t * 16 + r16;
+          a0[t] = act[stg][r * 8 + swz_slot(r, 2 * g)];
+          a1[t] = act[stg][r * 8 + swz_slot(r, 2 * g + 1)];
+        }
+        if (active) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.w0[j]),
+                                                                  __builtin_bit_cast(bf16x8, a0[t]), acc[j][t], 0, 0, 0);
+              acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.w1[j]),
+                                                                  __builtin_bit_cast(bf16x8, a1[t]), acc[j][t], 0, 0, 0);
+            }
+        }
+        // the next step's activations have landed (every wave waited for its
+        // own loads) and nobody reads this stage any more
+        MOE_WAIT_VMCNT(0);
+        __syncthreads();
+        cur = nxt;
+      }
+    }
+    seg_k0 += S.K;
+  }
+  if (!active) return;
+  const int epi = P.epi;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n_first + j * 16 + (lane >> 4) * 4;
+    if (n >= P.N) continue;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int m = t * 16 + (lane & 15);
+      if (m >= M) continue;
+      f32x4v v = acc[j][t];
+      if (partial != nullptr) {
+        *reinterpret_cast<f32x4v*>(partial + (int64_t)m * P.N + n) = v;
+      } else if (epi == EPI_F32) {
+        *reinterpret_cast<f32x4v*>(static_cast<float*>(P.C) + (int64_t)m * P.ldc + n) = v;
+      } else {
+        if (epi == EPI_RELU2_BF16) {
+          v[0] = relu2(v[0]); v[1] = relu2(v[1]); v[2] = relu2(v[2]); v[3] = relu2(v[3]);
+        }
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n) =
+            P.residual ? add_residual_bf16x4(v, P.residual + (int64_t)m * P.ldr + n)
+                       : u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    }
+  }
+}
+
 // One wavefront per (group, column block, k split); 4 waves per workgroup. A
 // column block is NSB slabs of 16 columns.
 // GROUPED_EPI: -1 for dense products (epilogue from the problem), else the
@@ -568,7 +717,11 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
   const dim3 grid((unsigned)((tasks + 3) / 4)), block(256);
   if (P.offsets == nullptr) {
     if (P.mx_codes != nullptr) return hipErrorInvalidValue;     // MX weights: grouped products only
-    if (P.f32_b != nullptr) {                                   // fp32 weights: one K segment
+    if (P.f32_b == nullptr && P.M > 32 && P.M <= 64 && MOE_SKINNY_DENSE64) {
+      // 33..64 rows, bf16 weights: the activations of a step shared through LDS
+      const int64_t wgs = (int64_t)((P.N + kDense64Cols - 1) / kDense64Cols) * P.ksplit;
+      hipLaunchKernelGGL(skinny_dense64_kernel, dim3((unsigned)wgs), dim3(256), 0, st, P);
+    } else if (P.f32_b != nullptr) {                                   // fp32 weights: one K segment
       if (P.nseg != 1) return hipErrorInvalidValue;
       if (nsb == 4) hipLaunchKernelGGL((skinny_kernel<4, -1, kSkinnyF32>), grid, block, 0, st, P);
       else hipLaunchKernelGGL((skinny_kernel<1, -1, kSkinnyF32>), grid, block, 0, st, P);
