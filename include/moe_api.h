@@ -153,7 +153,15 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* s
  *   ws  device workspace, >= moe_workspace_bytes(dims) bytes, 256-byte aligned;
  *       it keeps the intermediates listed in moe_ws_layout.
  * Intermediate roundings to bf16: z, h, y, y_lat, hs (the tensors the layer
- * stores in bf16); every sum is fp32. */
+ * stores in bf16); every sum is fp32.
+ * Asynchronous on `stream`. With T <= 64 the forward also uses a second stream
+ * of the library's (one per device, default priority, created on first use and
+ * kept): fc1 and the shared expert's up product run there beside the router,
+ * top-k and permutation, and `stream` waits for them before the expert
+ * products (on error returns too), so the caller still sees one stream's
+ * order, and a graph captured from `stream` takes both. Calls from several
+ * host threads on one device at once are correct (each call has its own fork
+ * and join events) and share that stream. */
 size_t moe_workspace_bytes(const moe_dims* dims);
 int moe_workspace_layout(const moe_dims* dims, moe_ws_layout* layout);
 int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out,

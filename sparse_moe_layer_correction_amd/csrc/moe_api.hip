@@ -405,34 +405,39 @@ size_t block_extra_bytes(const moe_dims& d) { return align_up((size_t)d.T * d.H 
 
 bool eps_ok(float eps) { return eps >= 0.f && eps <= 1e30f; }   // also rejects NaN
 
-// A second stream per device (default priority) and two events, created once:
-// a few-token forward runs fc1 and the shared expert's up product on it, beside
-// the router, top-k and permutation on the caller's stream (small,
-// latency-bound kernels), and joins it back before the expert products.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-const SideStream* side_stream() {
+// A second stream per device (default priority), created once: a few-token
+// forward runs fc1 and the shared expert's up product on it, beside the
+// router, top-k and permutation on the caller's stream (small, latency-bound
+// kernels), and joins it back before the expert products. The fork and join
+// events are the call's own (shared ones would let calls from two host threads
+// wait on each other's records).
+hipStream_t side_stream() {
   static std::mutex mu;
-  static SideStream per_dev[64];
+  static hipStream_t per_dev[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
-  SideStream& ss = per_dev[dev];
-  if (ss.s == nullptr) {
-    SideStream n;
-    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
-      if (n.fork) (void)hipEventDestroy(n.fork);
-      (void)hipStreamDestroy(n.s);
-      return nullptr;
-    }
-    ss = n;
+  if (per_dev[dev] == nullptr) {
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    per_dev[dev] = s;
   }
-  return &ss;
+  return per_dev[dev];
 }
+
+// the call's fork and join events (destroyed when the call returns; the
+// stream operations that use them are enqueued by then)
+struct SideEvents {
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool make() {
+    return hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess;
+  }
+  ~SideEvents() {
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
+  }
+};
 
 int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
                  size_t ws_bytes, hipStream_t stream, const Marks& mk, const moe_experts_mx* mx = nullptr,
@@ -490,7 +495,9 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   // its phases)
   const bool skinny = d.T <= kSkinnyMaxT;
   float* partial = skinny ? at<float>(ws, l.partial) : nullptr;
-  const SideStream* side = (skinny && mk.ev == nullptr) ? side_stream() : nullptr;
+  hipStream_t side = (skinny && mk.ev == nullptr) ? side_stream() : nullptr;
+  SideEvents sev;
+  if (side != nullptr && !sev.make()) side = nullptr;       // no events: everything on `stream`
   auto fc1_shared_up = [&](hipStream_t s, float* part) -> int {
     SkinnyProblem P = skinny_dense(d.T, d.L, d.L, z, L, EPI_BF16, d.H, part);
     add_seg(P, x, H, w->w_fc1, H, d.H);
@@ -502,23 +509,24 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   };
   // the caller's stream waits for the side stream's work on every way out,
   // errors included (that work writes into the workspace)
+  // (declared after sev, so it runs before the events are destroyed)
   struct Join {
-    const SideStream* side;
+    hipEvent_t ev;
     hipStream_t stream;
     bool armed = false;
     hipError_t now() {
       armed = false;
-      return hipStreamWaitEvent(stream, side->join, 0);
+      return hipStreamWaitEvent(stream, ev, 0);
     }
     ~Join() {
-      if (armed) (void)hipStreamWaitEvent(stream, side->join, 0);
+      if (armed) (void)hipStreamWaitEvent(stream, ev, 0);
     }
-  } join{side, stream};
+  } join{sev.join, stream};
   if (side != nullptr) {
-    if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+    if (hipEventRecord(sev.fork, stream) != hipSuccess || hipStreamWaitEvent(side, sev.fork, 0) != hipSuccess)
       return MOE_ERR_HIP;
-    const int rs = fc1_shared_up(side->s, at<float>(ws, l.partial2));
-    if (hipEventRecord(side->join, side->s) != hipSuccess) return MOE_ERR_HIP;
+    const int rs = fc1_shared_up(side, at<float>(ws, l.partial2));
+    if (hipEventRecord(sev.join, side) != hipSuccess) return MOE_ERR_HIP;
     join.armed = true;
     if (rs != MOE_OK) return rs;
   }
