@@ -35,11 +35,15 @@ constexpr int kSkinnyTargetWaves = MOE_SKINNY_TARGET_WAVES;
 // tokens from which the tiled router product splits K in two
 constexpr int kRouterSplitMinT = 4096;
 
-int skinny_ksplit(int N, int K, int M) {
+// bf16 products of 1-16 rows aim at twice as many waves: one token's products
+// gained about 1 % from it, while the fp32 router product lost (its waves
+// carry three times the bytes per column).
+int skinny_ksplit(int N, int K, int M, bool f32_weights = false) {
   if (N <= 0 || K < 64) return 1;
   const int width = M > 16 ? 64 : 16;      // columns per wave (see skinny_slabs_per_wave)
   const int slabs = (N + width - 1) / width;
-  int ks = (kSkinnyTargetWaves + slabs - 1) / slabs;
+  const int target = (M <= 16 && !f32_weights) ? 2 * kSkinnyTargetWaves : kSkinnyTargetWaves;
+  int ks = (target + slabs - 1) / slabs;
   // the fp32 partials are written once and read once: 8*ks*M*N bytes against
   // 2*N*K bytes of weights; keep them within the weight traffic (a quarter of
   // it left a 64-token decode's dense products with 64-256 waves: measured
@@ -138,7 +142,7 @@ Layout make_layout(const moe_dims& d) {
   if (T <= kSkinnyMaxT && L > 0 && I > 0 && Is > 0 && H > 0) {
     // split-K partials of the dense skinny products: [ksplit, T, N] fp32
     size_t p = 0;
-    p = std::max(p, (size_t)skinny_ksplit((int)l.ldl, (int)(3 * H), (int)T) * T * l.ldl * 4);
+    p = std::max(p, (size_t)skinny_ksplit((int)l.ldl, (int)(3 * H), (int)T, true) * T * l.ldl * 4);
     p = std::max(p, (size_t)skinny_ksplit((int)L, (int)H, (int)T) * T * L * 4);
     p = std::max(p, (size_t)skinny_ksplit((int)Is, (int)H, (int)T) * T * Is * 4);
     p = std::max(p, (size_t)skinny_ksplit((int)H, (int)(L + Is), (int)T) * T * H * 4);
@@ -188,7 +192,8 @@ void add_seg(SkinnyProblem& p, const uint16_t* A, int64_t lda, const uint16_t* B
 }
 
 // Dense skinny problem C[M, N] over a total reduction length Ktot.
-SkinnyProblem skinny_dense(int M, int N, int Nb, void* C, int64_t ldc, int epi, int Ktot, float* partial) {
+SkinnyProblem skinny_dense(int M, int N, int Nb, void* C, int64_t ldc, int epi, int Ktot, float* partial,
+                           bool f32_weights = false) {
   SkinnyProblem p{};
   p.M = M;
   p.N = N;
@@ -197,7 +202,7 @@ SkinnyProblem skinny_dense(int M, int N, int Nb, void* C, int64_t ldc, int epi, 
   p.C = C;
   p.ldc = ldc;
   p.epi = epi;
-  p.ksplit = skinny_ksplit(N, Ktot, M);
+  p.ksplit = skinny_ksplit(N, Ktot, M, f32_weights);
   p.partial = p.ksplit > 1 ? partial : nullptr;
   if (p.partial == nullptr) p.ksplit = 1;
   return p;
@@ -256,7 +261,7 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   const int64_t EH = (int64_t)d.E * d.H;
   if (mk.mark(MOE_PHASE_ROUTER_GEMM) != hipSuccess) return MOE_ERR_HIP;
   if (skinny) {
-    SkinnyProblem P = skinny_dense(d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32, d.H, partial);
+    SkinnyProblem P = skinny_dense(d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32, d.H, partial, true);
     add_seg(P, x, d.H, nullptr, d.H, d.H);
     P.f32_b = w_router;
     e = launch_skinny(P, st);
