@@ -267,17 +267,21 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
     e = launch_skinny(P, st);
   } else if (d.T >= kRouterSplitMinT && d.H % 128 == 0) {
     // Many tokens: K split in two (each half of H over the three weight parts)
-    // so that 256x256 tiles fill the CUs (E = 512 columns make only 2 column
-    // tiles); the top-k adds the halves' fp32 logits. Ultra prefill: 0.43 ms
-    // with 128x128 tiles over the whole K.
+    // so that more tiles fill the CUs (E = 512 columns make only 2 column
+    // tiles of 256); the top-k adds the halves' fp32 logits. Ultra prefill:
+    // 0.43 ms with 128x128 tiles over the whole K. Up to 128 experts take
+    // 128x128 tiles: a 256-wide tile would issue twice the work on padding
+    // columns with half as many workgroups (counters: 7-15 % MFMA busy at
+    // 4096-8192 tokens, E = 128).
     const int Hh = d.H / 2;
+    const int cfg = l.ldl <= 128 ? TILE_128x128 : TILE_256x256;
     GemmLaunch L{};
     L.np = 2;
     for (int h = 0; h < 2; ++h) {
-      L.p[h] = dense_problem(TILE_256x256, d.T, (int)l.ldl, d.E, logits + (int64_t)h * d.T * l.ldl, l.ldl, EPI_F32);
+      L.p[h] = dense_problem(cfg, d.T, (int)l.ldl, d.E, logits + (int64_t)h * d.T * l.ldl, l.ldl, EPI_F32);
       for (int s = 0; s < 3; ++s) add_seg(L.p[h], x + h * Hh, d.H, parts + s * EH + h * Hh, d.H, Hh);
     }
-    e = launch_gemm(L, TILE_256x256, st);
+    e = launch_gemm(L, cfg, st);
     logits2 = logits + (int64_t)d.T * l.ldl;
   } else {
     const int cfg = choose_dense_cfg(d.T, (int)l.ldl);

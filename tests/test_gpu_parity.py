@@ -62,6 +62,7 @@ def ws_view(ws, lay, name, dtype, shape):
     ("tiny", dict(K=1)),
     ("nano", dict(T=1024)),
     ("nano", dict(T=4096)),                  # from 4096 tokens the tiled router splits K in two
+    ("super", dict(T=4100)),                 # the same with 128-wide tiles (E = 128) and a ragged M tile
     ("super", dict(T=2048)),
     ("ultra_decode1", {}),
     ("ultra_decode64", {}),
