@@ -36,6 +36,22 @@ __global__ void split_router_weight_kernel(const float* __restrict__ w, int64_t 
   }
 }
 
+// Max of a 64-bit key over the wave. The keys of one top-K round are distinct
+// (the low word holds the expert index), so when a single lane holds the
+// largest high word its key is the answer and the second 32-bit reduction over
+// the low words can be skipped; it runs only on a tie of the high words.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  const uint32_t vh = (uint32_t)(v >> 32);
+  const uint32_t hi = wave_max_u32(vh);
+  const uint64_t holders = __ballot(vh == hi);
+  uint32_t lo;
+  if (__popcll(holders) == 1)
+    lo = __builtin_amdgcn_readlane((uint32_t)v, __builtin_amdgcn_readfirstlane(__ffsll((long long)holders) - 1));
+  else
+    lo = wave_max_u32(vh == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 template <int VPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
                                                    const float* __restrict__ logits2, int64_t ldl,
@@ -117,26 +133,41 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     admitted = topk_group * G;
   }
 
+  // Each lane sorts its keys in descending order once (a compare-exchange
+  // network with no dependence between the pairs of a pass), so the lane's
+  // candidate in a round is the head of its list, and a lane whose head wins
+  // shifts the list by one. A round is then one wave-wide max instead of a
+  // serial scan of the lane's keys followed by it.
+  uint64_t q[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) q[j] = key[j];
+#pragma unroll
+  for (int pass = 0; pass < VPL; ++pass) {
+#pragma unroll
+    for (int j = pass & 1; j + 1 < VPL; j += 2) {
+      const uint64_t a = q[j], b = q[j + 1];
+      q[j] = a > b ? a : b;
+      q[j + 1] = a > b ? b : a;
+    }
+  }
+
   uint32_t taken = 0;
   uint64_t kth = 0;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      if (!((taken >> j) & 1u) && key[j] > best) best = key[j];
-    best = wave_max_u64(best);
+    const uint64_t best = wave_max_key(q[0]);
     kth = best;
     const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    if ((e & 63) == lane) taken |= 1u << (e >> 6);
+    if (q[0] == best) {
+      taken |= 1u << (e >> 6);
+#pragma unroll
+      for (int j = 0; j + 1 < VPL; ++j) q[j] = q[j + 1];
+      q[VPL - 1] = 0;
+    }
   }
 
   float gapv = __builtin_inff();
   if (K < admitted) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      if (!((taken >> j) & 1u) && key[j] > best) best = key[j];
-    best = wave_max_u64(best);
+    const uint64_t best = wave_max_key(q[0]);
     gapv = f32_from_order_key((uint32_t)(kth >> 32)) - f32_from_order_key((uint32_t)(best >> 32));
   }
   gapv = fminf(gapv, ggap);
