@@ -63,6 +63,10 @@ def ws_view(ws, lay, name, dtype, shape):
     ("nano", dict(T=1024)),
     ("nano", dict(T=4096)),                  # from 4096 tokens the tiled router splits K in two
     ("super", dict(T=4100)),                 # the same with 128-wide tiles (E = 128) and a ragged M tile
+    ("tiny", dict(T=300, E=200, K=8)),       # 4 keys per lane, E not a multiple of 64
+    ("tiny", dict(T=300, E=1000, K=22)),     # 16 keys per lane (E > 512), ragged
+    ("tiny", dict(T=130, E=1024, K=64)),     # the largest E and K the library takes
+    ("tiny", dict(T=64, E=1000, K=22)),      # few-token router over 1000 experts
     ("super", dict(T=2048)),
     ("ultra_decode1", {}),
     ("ultra_decode64", {}),
