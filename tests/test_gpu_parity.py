@@ -270,6 +270,8 @@ def _sample(T, n, seed):
 @pytest.mark.parametrize("name,over,n", [
     ("nano", dict(T=1024), 6),
     ("super", dict(T=2048), 6),
+    ("nano", {}, 4),                         # the benchmarked sizes: K-split router with 128-wide tiles
+    ("super", {}, 4),
     ("ultra_decode1", {}, 1),
     ("ultra_decode64", {}, 3),
     ("ultra_prefill", {}, 3),
