@@ -230,6 +230,8 @@ def _compare_tokens(d, out, ws, lay, tokens, idx_gpu, label):
                                        # about 175 / 287 rows per expert: expert tails of 129-192
                                        # rows (three-quarter-height tiles) / full plus short tails
                                        ("tiny", dict(T=700, E=4, K=1)), ("tiny", dict(T=1150, E=4, K=1)),
+                                       # about 270 rows per expert: tails of at most 64 rows
+                                       ("tiny", dict(T=1080, E=4, K=1)),
                                        # 32 experts x about 256 rows x 4 column tiles: 128 grouped
                                        # tiles, so each XCD's last eighth is claimed through its
                                        # counter (every output and intermediate row checked)
