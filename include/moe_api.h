@@ -121,8 +121,9 @@ typedef struct moe_ws_layout {
  * The logits are accumulated in fp32 from exact bf16 x fp32 products (the fp32
  * weight is split exactly into three bf16 parts: by a pass over the weight for
  * the tiled product, in registers for forwards of at most 64 tokens; from 4096
- * tokens the tiled product sums the two halves of H separately and adds them);
- * only the summation order differs from an exact fp32 dot product. */
+ * tokens the tiled product sums the two halves of H separately and adds them,
+ * and with at most 128 experts it also sums each weight part separately); only
+ * the summation order differs from an exact fp32 dot product. */
 size_t moe_route_workspace_bytes(const moe_dims* dims);
 int moe_route(const moe_dims* dims, const uint16_t* x, const float* w_router,
               const float* corr_bias, int32_t* topk_idx, float* topk_gate, float* topk_gap,

@@ -75,7 +75,8 @@ struct PermuteScratch {
 
 hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* parts, hipStream_t st);
 // logits2: nullable, the second half of a K-split router product, added to logits
-hipError_t launch_topk(const float* logits, const float* logits2, int64_t ldl, const float* bias, int T, int E, int K,
+hipError_t launch_topk(const float* logits, const float* logits2, int64_t ldl, int nparts, int64_t part_off,
+                       const float* bias, int T, int E, int K,
                        float scale, int n_group, int topk_group, int32_t* idx, float* gate, float* gap, hipStream_t st);
 hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, const PermuteScratch& ps,
                                int32_t* offsets, int32_t* row_token, int32_t* slot_row, hipStream_t st);

@@ -106,6 +106,18 @@ moe_dims only_used(const moe_dims& d, int use) {
   return u;
 }
 
+// The tiled router product from kRouterSplitMinT tokens splits K in two. With
+// at most 128 experts (E a multiple of 64) it also takes the three bf16 parts
+// of the weight as 3E output columns instead of three K segments of one
+// accumulator (the parts are stored one after the other, so their rows are one
+// [3E, H] matrix): three times the workgroups, each a third of the k steps.
+// The top-k adds the 2 x 3 partial logits. (E = 128 gives only T/128 x 2
+// workgroups otherwise: 7-14 % MFMA busy at 4096-8192 tokens.)
+bool router_splits_k(int64_t T, int64_t H) { return T >= kRouterSplitMinT && H % 128 == 0; }
+bool router_stacks_parts(int64_t T, int64_t H, int64_t E) {
+  return router_splits_k(T, H) && E <= 128 && E % 64 == 0;
+}
+
 Layout make_layout(const moe_dims& d) {
   Layout l{};
   const int64_t T = d.T, H = d.H, L = d.L, E = d.E, I = d.I, K = d.K, Is = d.Is, TK = T * K;
@@ -115,7 +127,8 @@ Layout make_layout(const moe_dims& d) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   l.wsplit = take(3 * E * H * 2);
-  l.logits = take(2 * T * l.ldl * 4);           // two halves when the router product splits K
+  // two halves when the router product splits K, each 3 column blocks when it stacks the weight parts
+  l.logits = take(2 * T * l.ldl * 4 * (router_stacks_parts(T, H, E) ? 3 : 1));
   l.route_end = o;
   l.permute_begin = o;
   l.masks = take(E * l.nblk * 8);
@@ -250,6 +263,8 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   uint16_t* parts = at<uint16_t>(ws, l.wsplit);
   float* logits = at<float>(ws, l.logits);
   const float* logits2 = nullptr;
+  int64_t ldl = l.ldl;                       // row length of the logits the top-k reads
+  int nparts = 1;                            // column blocks of E summed per half (stacked parts)
   const bool skinny = d.T <= kSkinnyMaxT && partial != nullptr;
   hipError_t e = hipSuccess;
   if (mk.mark(MOE_PHASE_ROUTER_SPLIT) != hipSuccess) return MOE_ERR_HIP;
@@ -265,7 +280,7 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
     add_seg(P, x, d.H, nullptr, d.H, d.H);
     P.f32_b = w_router;
     e = launch_skinny(P, st);
-  } else if (d.T >= kRouterSplitMinT && d.H % 128 == 0) {
+  } else if (router_splits_k(d.T, d.H)) {
     // Many tokens: K split in two (each half of H over the three weight parts)
     // so that more tiles fill the CUs (E = 512 columns make only 2 column
     // tiles of 256); the top-k adds the halves' fp32 logits. Ultra prefill:
@@ -275,14 +290,21 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
     // 4096-8192 tokens, E = 128).
     const int Hh = d.H / 2;
     const int cfg = l.ldl <= 128 ? TILE_128x128 : TILE_256x256;
+    const bool stack = router_stacks_parts(d.T, d.H, d.E);
+    if (stack) {
+      ldl = 3 * (int64_t)d.E;
+      nparts = 3;
+    }
     GemmLaunch L{};
     L.np = 2;
     for (int h = 0; h < 2; ++h) {
-      L.p[h] = dense_problem(cfg, d.T, (int)l.ldl, d.E, logits + (int64_t)h * d.T * l.ldl, l.ldl, EPI_F32);
-      for (int s = 0; s < 3; ++s) add_seg(L.p[h], x + h * Hh, d.H, parts + s * EH + h * Hh, d.H, Hh);
+      L.p[h] = dense_problem(cfg, d.T, (int)ldl, stack ? (int)ldl : d.E, logits + (int64_t)h * d.T * ldl, ldl, EPI_F32);
+      if (stack) add_seg(L.p[h], x + h * Hh, d.H, parts + h * Hh, d.H, Hh);
+      else
+        for (int s = 0; s < 3; ++s) add_seg(L.p[h], x + h * Hh, d.H, parts + s * EH + h * Hh, d.H, Hh);
     }
     e = launch_gemm(L, cfg, st);
-    logits2 = logits + (int64_t)d.T * l.ldl;
+    logits2 = logits + (int64_t)d.T * ldl;
   } else {
     const int cfg = choose_dense_cfg(d.T, (int)l.ldl);
     GemmLaunch L{};
@@ -293,7 +315,7 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (mk.mark(MOE_PHASE_TOPK) != hipSuccess) return MOE_ERR_HIP;
-  e = launch_topk(logits, logits2, l.ldl, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d), topk_groups_of(d), idx, gate,
+  e = launch_topk(logits, logits2, ldl, nparts, d.E, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d), topk_groups_of(d), idx, gate,
                   gap, st);
   return hip_status(e);
 }

@@ -55,6 +55,7 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
 template <int VPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
                                                    const float* __restrict__ logits2, int64_t ldl,
+                                                   int nparts, int64_t part_off,
                                                    const float* __restrict__ bias, int T, int E, int K,
                                                    float scale, int n_group, int topk_group,
                                                    int32_t* __restrict__ idx, float* __restrict__ gate,
@@ -73,7 +74,14 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     s[j] = 0.f;
     key[j] = 0;
     if (e < E) {
-      const float l = lrow2 ? lrow[e] + lrow2[e] : lrow[e];
+      // a half's logit is the sum of its nparts column blocks (stacked weight parts), in order
+      float l = lrow[e];
+      for (int p = 1; p < nparts; ++p) l += lrow[p * part_off + e];
+      if (lrow2) {
+        float l2 = lrow2[e];
+        for (int p = 1; p < nparts; ++p) l2 += lrow2[p * part_off + e];
+        l += l2;
+      }
       const float sv = 1.0f / (1.0f + expf(-l));
       const float cv = sv + bias[e];
       s[j] = sv;
@@ -201,13 +209,14 @@ hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* pa
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const float* logits2, int64_t ldl, const float* bias, int T, int E, int K,
+hipError_t launch_topk(const float* logits, const float* logits2, int64_t ldl, int nparts, int64_t part_off,
+                       const float* bias, int T, int E, int K,
                        float scale, int n_group, int topk_group, int32_t* idx, float* gate, float* gap,
                        hipStream_t st) {
   const dim3 grid((T + 3) / 4), block(256);
   const int vpl = (E + 63) / 64;
 #define MOE_TOPK(V)                                                                                           \
-  hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, st, logits, logits2, ldl, bias, T, E, K, scale, n_group,   \
+  hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, st, logits, logits2, ldl, nparts, part_off, bias, T, E, K, scale, n_group,   \
                      topk_group, idx, gate, gap)
   if (vpl <= 1) MOE_TOPK(1);
   else if (vpl <= 2) MOE_TOPK(2);
