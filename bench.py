@@ -85,15 +85,18 @@ def cpu_baseline(d, cfg, idx_gpu, n_tokens: int, experts_fmt: str = "bf16"):
 
     args = (u(d["x"][tokens]), d["w_router"].cpu().numpy(), d["corr_bias"].cpu().numpy(), u(d["w_fc1"]),
             u(d["w_fc2"]), u(d["w_sh_up"]), u(d["w_sh_down"]))
-    t0 = time.perf_counter()
-    oracle.forward(*args, expert, cfg.K, cfg.routed_scaling, mirror=True)
-    dt = time.perf_counter() - t0
-    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    dts = {}
+    for name, dt in (("f64", np.float64), ("f32", np.float32)):
+        t0 = time.perf_counter()
+        oracle.forward(*args, expert, cfg.K, cfg.routed_scaling, mirror=True, dtype=dt)
+        dts[name] = time.perf_counter() - t0
+    return {"value": len(tokens) / dts["f64"], "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "value_fp32": len(tokens) / dts["f32"],
             "sample": f"{len(tokens)} of the {cfg.T} tokens of the {cfg.name} batch (tokens are independent), "
-                      f"whole layer per token in float64 with bf16 rounding"
+                      f"whole layer per token with bf16 rounding"
                       f"{f' ({experts_fmt.upper()} experts, dequantised)' if experts_fmt != 'bf16' else ''}; "
-                      f"{dt:.1f} s on "
-                      f"{os.cpu_count()} host cores, BLAS threads {threads}"}
+                      f"float64 (parity mode, `value`) {dts['f64']:.1f} s, float32 (`value_fp32`) "
+                      f"{dts['f32']:.1f} s, on {os.cpu_count()} host cores, BLAS threads {threads}"}
 
 
 def graph_ms_per_step(fwd, steps: int) -> float:
@@ -160,7 +163,8 @@ def block_timing(M, d, weights, cfg, args, mx, ws, lay):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed forwards (default 20; 200 for the few-token workloads)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ultra_prefill",
                     choices=["ultra_prefill", "ultra_decode64", "ultra_decode1", "nano", "super", "tiny"])
@@ -187,6 +191,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     cfg = W.get_config(args.workload)
+    if args.steps is None:
+        args.steps = 200 if cfg.T <= 64 else 20
+    args.warmup = max(args.warmup, 3)
     d = W.make_inputs(cfg, device="cuda")
     weights = {k: v for k, v in d.items() if k != "x"}
     dims = M.dims_from(d["x"], weights, cfg.K, cfg.routed_scaling)
@@ -218,13 +225,19 @@ def main():
         fwd()
     torch.cuda.synchronize()
 
+    # K timed forwards, a HIP event on the forward's stream between steps (the
+    # per-step distribution); ms_per_step is the host clock over all K
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    marks[0].record(stream)
     for i in range(args.steps):
         fwd()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
     # the phases: as many steps again through the profiled forward, which runs
     # every phase on the one stream between HIP events (the plain forward runs
@@ -303,6 +316,10 @@ def main():
         "near_tie_tokens": near_ties,
         "grouped_m_tiles": m_tiles,
         "grouped_row_padding": round(1 - cfg.T * cfg.K / max(1, m_tiles * 256), 4),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4),
+                    "mean": round(float(step_ms.mean()), 4), "n": int(step_ms.size)},
         "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "events_ms_per_step": round(ev_ms, 4),
         "roofline": roofline,

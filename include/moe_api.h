@@ -133,11 +133,12 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const float* w_router,
  * an expert -- the rows a loop over the hit experts gathers (QA Q5.6) -- and
  * gather rows of `src` into that order. Reads T, E, K of dims (the other
  * fields are ignored). Entries of topk_idx outside [0,E) are skipped and their
- * slot_row is set to -1 (rows past the valid count are then left unwritten).
+ * slot_row is set to -1: the valid rows are then [0, off[E]) and, past them,
+ * row_token is left unwritten and dst holds zero rows.
  *   topk_idx       device [T,K] int32, values in [0,E), distinct within a token
  *   src            device [T,C] bf16 (may be NULL together with dst: maps only)
  *   C              row length of src/dst in elements, a multiple of 8
- *   dst            device [T*K, C] bf16 out: dst[r] = src[row_token[r]]
+ *   dst            device [T*K, C] bf16 out: dst[r] = src[row_token[r]] for r < off[E], else 0
  *   expert_offsets device [E+1] int32 out: rows of expert e are [off[e], off[e+1])
  *   row_token      device [T*K] int32 out: token of permuted row r
  *   slot_row       device [T*K] int32 out: permuted row of slot (t,k), index t*K+k
@@ -155,14 +156,9 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* s
  *       it keeps the intermediates listed in moe_ws_layout.
  * Intermediate roundings to bf16: z, h, y, y_lat, hs (the tensors the layer
  * stores in bf16); every sum is fp32.
- * Asynchronous on `stream`. With T <= 64 the forward also uses a second stream
- * of the library's (one per device, default priority, created on first use and
- * kept): fc1 and the shared expert's up product run there beside the router,
- * top-k and permutation, and `stream` waits for them before the expert
- * products (on error returns too), so the caller still sees one stream's
- * order, and a graph captured from `stream` takes both. Calls from several
- * host threads on one device at once are correct (each call has its own fork
- * and join events) and share that stream. */
+ * Every kernel of the call runs on `stream`, in order; the library creates no
+ * stream or event. Calls from several host threads are independent as long as
+ * they use different workspaces and outputs. */
 size_t moe_workspace_bytes(const moe_dims* dims);
 int moe_workspace_layout(const moe_dims* dims, moe_ws_layout* layout);
 int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out,

@@ -26,12 +26,17 @@ Readings where the pages leave a step open (each listed in the design notes):
   * the router reads the uncompressed x (QA Q5.2 flattens to hidden_size);
   * expert groups: WT "路由与共享专家" says the top-K is taken within groups,
     and QA CH9 Q9.2 has the MoE inherit DeepseekV3MoE's routing, but no page
-    gives a group count or the group rule. ``route`` takes n_group /
-    topk_group (default 1 / 1: top-K over all E experts) and follows the
-    DeepSeek-V3 rule of that parent: experts form n_group equal contiguous
-    groups, a group scores the sum of its two highest choice scores (of its
-    one score if it has one expert), the topk_group best groups (ties: lower
-    group index) admit their experts, and the top-K is taken among those;
+    gives a group count, how experts are grouped or how a group is scored.
+    ``route`` takes n_group / topk_group (default 1 / 1: top-K over all E
+    experts, the only setting the pages' workloads use) and, for n_group > 1,
+    follows the DeepSeek-V3 rule of that parent, which comes from outside the
+    pages: experts form n_group equal contiguous groups, a group scores the sum
+    of its two highest choice scores (its one score if it has one expert), the
+    topk_group best groups (ties: lower group index) admit their experts, and
+    the top-K is taken among those. PARITY UNPINNED for that group ranking: no
+    page fixes it, so no test can check it against a fact. The pins check the
+    subset search given the ranking, that admitting every group is the plain
+    top-K, and that the choice stays inside the admitted groups;
   * dropless: every (token, expert) pair is computed;
   * ties in the choice score go to the lower expert index;
   * a token's K experts are reported in ascending expert order (the sum over
@@ -96,21 +101,22 @@ class RouteResult:
 
 
 def route(x: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray, K: int,
-          routed_scaling: float, n_group: int = 1, topk_group: int = 1) -> RouteResult:
+          routed_scaling: float, n_group: int = 1, topk_group: int = 1, dtype=np.float64) -> RouteResult:
     """Router of QA Q5.2 / Q5.3 with the gate rule of WT "路由与共享专家" and QA Q5.8.
 
     x: [T,H] float64 (bf16 values); w_router: [E,H] (fp32 values); corr_bias: [E].
     n_group / topk_group: group-limited selection (module docstring); 1 / 1 is
-    the plain top-K over all experts.
+    the plain top-K over all experts. dtype: the arithmetic type (float64, the
+    parity mode; float32 only to time the same code at single precision).
 
     gap[t] is the smallest margin that decides token t's routing: the K-th
     minus the (K+1)-th choice score among the admitted experts, and, with
     groups, the topk_group-th minus the next group score (inf when nothing
     follows).
     """
-    x = np.asarray(x, dtype=np.float64)
-    wr = np.asarray(w_router, dtype=np.float64)
-    b = np.asarray(corr_bias, dtype=np.float64)
+    x = np.asarray(x, dtype=dtype)
+    wr = np.asarray(w_router, dtype=dtype)
+    b = np.asarray(corr_bias, dtype=dtype)
     T = x.shape[0]
     E = wr.shape[0]
     assert np.all(np.isfinite(x)) and np.all(np.isfinite(wr)) and np.all(np.isfinite(b))
@@ -203,7 +209,8 @@ def forward(x_bits: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray,
             expert: Callable[[int], Tuple[np.ndarray, np.ndarray]],
             K: int, routed_scaling: float, mirror: bool = True,
             idx_override: Optional[np.ndarray] = None,
-            keep: bool = False, n_group: int = 1, topk_group: int = 1) -> Dict[str, np.ndarray]:
+            keep: bool = False, n_group: int = 1, topk_group: int = 1,
+            dtype=np.float64) -> Dict[str, np.ndarray]:
     """One forward of the layer on the tokens in ``x_bits`` (tokens are independent).
 
     x_bits [T,H] and the *_bits weights are bf16 bit patterns (uint16);
@@ -215,14 +222,26 @@ def forward(x_bits: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray,
     stated rule on the unbiased scores of those experts); it is used to follow
     another party's choice on near-tie tokens.
 
+    ``dtype`` is the arithmetic type: float64 is the parity mode; float32 runs
+    the same steps at single precision (used only to time the oracle at that
+    precision; every parity comparison uses float64).
+
     Returns out [T,H] (float64; bf16 values when mirror) plus the route and
     permutation results; with ``keep`` also z, h, y, y_lat, hs.
     """
-    rnd = round_bf16 if mirror else _identity
-    x = bf16_bits_to_f64(x_bits)
+    if mirror:
+        def rnd(a):
+            return round_bf16(a).astype(dtype)
+    else:
+        rnd = _identity
+
+    def dec(bits):
+        return bf16_bits_to_f64(bits).astype(dtype)
+
+    x = dec(x_bits)
     T, H = x.shape
     E = np.asarray(w_router).shape[0]
-    r = route(x, w_router, corr_bias, K, routed_scaling, n_group, topk_group)
+    r = route(x, w_router, corr_bias, K, routed_scaling, n_group, topk_group, dtype=dtype)
     if idx_override is not None:
         idx = np.sort(np.asarray(idx_override, dtype=np.int64), axis=1).astype(np.int32)
         assert idx.shape == (T, K)
@@ -234,35 +253,34 @@ def forward(x_bits: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray,
     p = permute(r.idx, E)
 
     # fc1_latent_proj: compress to the latent (QA Q5.1)
-    z = rnd(x @ bf16_bits_to_f64(w_fc1_bits).T)
+    z = rnd(x @ dec(w_fc1_bits).T)
     L = z.shape[1]
 
     # routed experts over the latent, one expert's rows at a time
-    y = np.zeros((T * K, L), dtype=np.float64)
+    y = np.zeros((T * K, L), dtype=dtype)
     hs_list = {}
     for e in range(E):
         a, b = int(p.offsets[e]), int(p.offsets[e + 1])
         if a == b:
             continue
         wu_bits, wd_bits = expert(e)
-        h_e, y_e = expert_mlp(z[p.row_token[a:b]], bf16_bits_to_f64(wu_bits),
-                              bf16_bits_to_f64(wd_bits), rnd)
+        h_e, y_e = expert_mlp(z[p.row_token[a:b]], dec(wu_bits), dec(wd_bits), rnd)
         y[a:b] = y_e
         if keep:
             hs_list[e] = h_e
 
     # gate each expert output, then sum in the latent (QA Q5.5 point 3)
-    gate64 = r.gate.astype(np.float64)
-    y_lat = np.zeros((T, L), dtype=np.float64)
+    gate64 = r.gate.astype(dtype)
+    y_lat = np.zeros((T, L), dtype=dtype)
     for j in range(K):
         y_lat += gate64[:, j:j + 1] * y[p.slot_row[:, j]]
     y_lat = rnd(y_lat)
 
     # shared expert on the uncompressed input (QA Q5.7)
-    hs = rnd(_relu2(x @ bf16_bits_to_f64(w_sh_up_bits).T))
+    hs = rnd(_relu2(x @ dec(w_sh_up_bits).T))
 
     # fc2_latent_proj plus the shared expert, one rounding at the end (QA Q5.1)
-    out = rnd(y_lat @ bf16_bits_to_f64(w_fc2_bits).T + hs @ bf16_bits_to_f64(w_sh_down_bits).T)
+    out = rnd(y_lat @ dec(w_fc2_bits).T + hs @ dec(w_sh_down_bits).T)
 
     res = dict(out=out, idx=r.idx, gate=r.gate, gap=r.gap, counts=p.counts,
                offsets=p.offsets, row_token=p.row_token, slot_row=p.slot_row)
@@ -270,7 +288,7 @@ def forward(x_bits: np.ndarray, w_router: np.ndarray, corr_bias: np.ndarray,
         h = None
         if hs_list:
             I = next(iter(hs_list.values())).shape[1]
-            h = np.zeros((T * K, I), dtype=np.float64)
+            h = np.zeros((T * K, I), dtype=dtype)
             for e, h_e in hs_list.items():
                 h[p.offsets[e]:p.offsets[e + 1]] = h_e
         res.update(z=z, h=h, y=y, y_lat=y_lat, hs=hs, logits=r.logits, score=r.score,

@@ -116,11 +116,13 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2_t));
 }
 
-// Buffer resource over [base, base + 4 GiB): raw (stride 0) descriptor, word 3
-// as the gfx9 family expects for untyped loads.
-// num_records 0 makes every lane out of range: the load then touches no memory
-// (buffer range checking returns zeros).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_records = 0x7FFFFFFF) {
+// Buffer resource over [base, base + 2^32 - 1): raw (stride 0) descriptor, word 3
+// as the gfx9 family expects for untyped loads. A raw buffer access is in range
+// while its byte offset is below num_records, so -1 (0xFFFFFFFF) admits every
+// 32-bit offset but the last; num_records 0 makes every lane out of range: the
+// load then touches no memory (buffer range checking returns zeros).
+constexpr int kRsrcAll = -1;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_records = kRsrcAll) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, 0x00020000);
 }
 
@@ -317,7 +319,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
         point(seg);
       }
       const int so = (kt - seg_k0) * BK * 2;
-      const int nrec = live ? 0x7FFFFFFF : 0;
+      const int nrec = live ? kRsrcAll : 0;
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, nrec), rb = make_rsrc(bbase, nrec);
       // (the explicit casts of the lane offsets matter: without them the host
       // pass silently drops this kernel's launch stub)

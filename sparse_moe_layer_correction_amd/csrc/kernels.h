@@ -80,8 +80,9 @@ hipError_t launch_topk(const float* logits, const float* logits2, int64_t ldl, i
                        float scale, int n_group, int topk_group, int32_t* idx, float* gate, float* gap, hipStream_t st);
 hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, const PermuteScratch& ps,
                                int32_t* offsets, int32_t* row_token, int32_t* slot_row, hipStream_t st);
-hipError_t launch_gather_rows(const uint16_t* src, int C, const int32_t* row_token, int64_t rows, uint16_t* dst,
-                              hipStream_t st);
+// n_valid: device scalar, the number of rows the maps filled (offsets[E]); rows past it are zeroed
+hipError_t launch_gather_rows(const uint16_t* src, int C, const int32_t* row_token, const int32_t* n_valid,
+                              int64_t rows, uint16_t* dst, hipStream_t st);
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, int64_t T, int H, float eps, uint16_t* y,
                           hipStream_t st);
 hipError_t launch_bias_update(const int32_t* offsets, int E, float eta, float* bias, hipStream_t st);

@@ -5,8 +5,6 @@
 
 #include <string.h>
 
-#include <mutex>
-
 #include "kernels.h"
 
 namespace {
@@ -59,7 +57,7 @@ struct Layout {
   // permute
   size_t masks, base, counts, tile_info, n_mtiles, touched, n_touched, gemm_ctr;
   // forward
-  size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial, partial2;
+  size_t idx, gate, gap, offsets, row_token, slot_row, z, hs, h, y, y_lat, partial;
   size_t route_end, permute_begin, permute_end, total;
   int64_t ldl;         // logits row stride (E rounded up to 64)
   int nblk;            // token blocks of 64
@@ -126,7 +124,10 @@ Layout make_layout(const moe_dims& d) {
   l.max_mtiles = (int)(TK / kGroupedBM + E + 1);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
-  l.wsplit = take(3 * E * H * 2);
+  // a forward of at most kSkinnyMaxT tokens splits the router weight in
+  // registers (no parts); moe_route (L = I = Is = 0 here) always tiles
+  const bool few = T <= kSkinnyMaxT && L > 0 && I > 0 && Is > 0 && H > 0;
+  l.wsplit = take(few ? 0 : 3 * E * H * 2);
   // two halves when the router product splits K, each 3 column blocks when it stacks the weight parts
   l.logits = take(2 * T * l.ldl * 4 * (router_stacks_parts(T, H, E) ? 3 : 1));
   l.route_end = o;
@@ -152,7 +153,7 @@ Layout make_layout(const moe_dims& d) {
   l.y = take(TK * L * 2);
   l.y_lat = take(T * L * 2);
   l.partial = o;
-  if (T <= kSkinnyMaxT && L > 0 && I > 0 && Is > 0 && H > 0) {
+  if (few) {
     // split-K partials of the dense skinny products: [ksplit, T, N] fp32
     size_t p = 0;
     p = std::max(p, (size_t)skinny_ksplit((int)l.ldl, (int)(3 * H), (int)T, true) * T * l.ldl * 4);
@@ -160,12 +161,6 @@ Layout make_layout(const moe_dims& d) {
     p = std::max(p, (size_t)skinny_ksplit((int)Is, (int)H, (int)T) * T * Is * 4);
     p = std::max(p, (size_t)skinny_ksplit((int)H, (int)(L + Is), (int)T) * T * H * 4);
     take(p);
-    // fc1 and the shared up run on a second stream beside the router: partials of their own
-    l.partial2 = o;
-    take(std::max((size_t)skinny_ksplit((int)L, (int)H, (int)T) * T * L * 4,
-                  (size_t)skinny_ksplit((int)Is, (int)H, (int)T) * T * Is * 4));
-  } else {
-    l.partial2 = o;
   }
   l.total = o;
   return l;
@@ -333,7 +328,7 @@ PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 103; }
+int moe_abi_version(void) { return 104; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -415,7 +410,8 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_idx, const uint16_t* s
                                      permute_scratch(l, ws, l.permute_begin),
                                      expert_offsets, row_token, slot_row, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  if (src != nullptr) e = launch_gather_rows(src, C, row_token, (int64_t)dims->T * dims->K, dst, stream);
+  if (src != nullptr)
+    e = launch_gather_rows(src, C, row_token, expert_offsets + dims->E, (int64_t)dims->T * dims->K, dst, stream);
   return hip_status(e);
 }
 
@@ -435,40 +431,6 @@ struct BlockArgs {
 size_t block_extra_bytes(const moe_dims& d) { return align_up((size_t)d.T * d.H * 2); }
 
 bool eps_ok(float eps) { return eps >= 0.f && eps <= 1e30f; }   // also rejects NaN
-
-// A second stream per device (default priority), created once: a few-token
-// forward runs fc1 and the shared expert's up product on it, beside the
-// router, top-k and permutation on the caller's stream (small, latency-bound
-// kernels), and joins it back before the expert products. The fork and join
-// events are the call's own (shared ones would let calls from two host threads
-// wait on each other's records).
-hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t per_dev[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (per_dev[dev] == nullptr) {
-    hipStream_t s = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    per_dev[dev] = s;
-  }
-  return per_dev[dev];
-}
-
-// the call's fork and join events (destroyed when the call returns; the
-// stream operations that use them are enqueued by then)
-struct SideEvents {
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool make() {
-    return hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess;
-  }
-  ~SideEvents() {
-    if (fork) (void)hipEventDestroy(fork);
-    if (join) (void)hipEventDestroy(join);
-  }
-};
 
 int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out, void* ws,
                  size_t ws_bytes, hipStream_t stream, const Marks& mk, const moe_experts_mx* mx = nullptr,
@@ -521,46 +483,9 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   uint16_t* y = at<uint16_t>(ws, l.y);
   uint16_t* y_lat = at<uint16_t>(ws, l.y_lat);
 
-  // 1. router; few tokens: fc1 and the shared up on the side stream meanwhile
-  // (the profiled forward keeps one stream, so that its phase marks bound
-  // its phases)
+  // 1. router
   const bool skinny = d.T <= kSkinnyMaxT;
   float* partial = skinny ? at<float>(ws, l.partial) : nullptr;
-  hipStream_t side = (skinny && mk.ev == nullptr) ? side_stream() : nullptr;
-  SideEvents sev;
-  if (side != nullptr && !sev.make()) side = nullptr;       // no events: everything on `stream`
-  auto fc1_shared_up = [&](hipStream_t s, float* part) -> int {
-    SkinnyProblem P = skinny_dense(d.T, d.L, d.L, z, L, EPI_BF16, d.H, part);
-    add_seg(P, x, H, w->w_fc1, H, d.H);
-    if (launch_skinny(P, s) != hipSuccess) return MOE_ERR_HIP;
-    SkinnyProblem Q = skinny_dense(d.T, d.Is, d.Is, hs, Is, EPI_RELU2_BF16, d.H, part);
-    add_seg(Q, x, H, w->w_sh_up, H, d.H);
-    if (launch_skinny(Q, s) != hipSuccess) return MOE_ERR_HIP;
-    return MOE_OK;
-  };
-  // the caller's stream waits for the side stream's work on every way out,
-  // errors included (that work writes into the workspace)
-  // (declared after sev, so it runs before the events are destroyed)
-  struct Join {
-    hipEvent_t ev;
-    hipStream_t stream;
-    bool armed = false;
-    hipError_t now() {
-      armed = false;
-      return hipStreamWaitEvent(stream, ev, 0);
-    }
-    ~Join() {
-      if (armed) (void)hipStreamWaitEvent(stream, ev, 0);
-    }
-  } join{sev.join, stream};
-  if (side != nullptr) {
-    if (hipEventRecord(sev.fork, stream) != hipSuccess || hipStreamWaitEvent(side, sev.fork, 0) != hipSuccess)
-      return MOE_ERR_HIP;
-    const int rs = fc1_shared_up(side, at<float>(ws, l.partial2));
-    if (hipEventRecord(sev.join, side) != hipSuccess) return MOE_ERR_HIP;
-    join.armed = true;
-    if (rs != MOE_OK) return rs;
-  }
   int rc = run_route(d, l, x, w->w_router, w->corr_bias, idx, gate, at<float>(ws, l.gap), ws, stream, mk, partial);
   if (rc != MOE_OK) return rc;
 
@@ -573,12 +498,12 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
   // 3. x read by one launch for fc1 (z) and the shared expert's up + relu^2 (hs)
   if (skinny) {
     if (mk.mark(MOE_PHASE_FC1_SHARED_UP) != hipSuccess) return MOE_ERR_HIP;
-    if (side != nullptr) {
-      if (join.now() != hipSuccess) return MOE_ERR_HIP;
-    } else {
-      const int rs = fc1_shared_up(stream, partial);
-      if (rs != MOE_OK) return rs;
-    }
+    SkinnyProblem P = skinny_dense(d.T, d.L, d.L, z, L, EPI_BF16, d.H, partial);
+    add_seg(P, x, H, w->w_fc1, H, d.H);
+    if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
+    SkinnyProblem Q = skinny_dense(d.T, d.Is, d.Is, hs, Is, EPI_RELU2_BF16, d.H, partial);
+    add_seg(Q, x, H, w->w_sh_up, H, d.H);
+    if (launch_skinny(Q, stream) != hipSuccess) return MOE_ERR_HIP;
   } else {
     const int cfg = choose_dense_cfg(d.T, std::min(d.L, d.Is));
     GemmLaunch G{};

@@ -11,7 +11,8 @@
 //     out the M-tile table of the grouped expert products.
 //  4. scatter: slot (t,k) of expert e goes to row
 //       offsets[e] + base[e][t/64] + popcount(mask[e][t/64] below bit t%64).
-//  5. gather: dst[r] = src[row_token[r]] with 16-byte loads and stores.
+//  5. gather: dst[r] = src[row_token[r]] with 16-byte loads and stores (rows
+//     past offsets[E] -- slots of skipped entries -- are zero).
 // With at most 64 tokens, steps 1-4 run as one workgroup (permute_small_kernel).
 #include "kernels.h"
 
@@ -153,18 +154,23 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   slot_row[s] = r;
 }
 
+// Rows at or past *n_valid (the slots of entries outside [0, E), for which the
+// maps leave row_token unwritten) are written as zeros and read nothing.
 __global__ void __launch_bounds__(256) gather_rows_kernel(const uint16_t* __restrict__ src, int C,
                                                           const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ n_valid,
                                                           int64_t rows, uint16_t* __restrict__ dst) {
   const int cpr = C / 8;                      // 16-byte chunks per row
   const int64_t n = rows * cpr;
+  const int64_t valid = *n_valid;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (; i < n; i += stride) {
     const int64_t r = i / cpr;
     const int ch = (int)(i - r * cpr);
-    const int t = row_token[r];
-    reinterpret_cast<u32x4*>(dst + r * C)[ch] = reinterpret_cast<const u32x4*>(src + (int64_t)t * C)[ch];
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (r < valid) v = reinterpret_cast<const u32x4*>(src + (int64_t)row_token[r] * C)[ch];
+    reinterpret_cast<u32x4*>(dst + r * C)[ch] = v;
   }
 }
 
@@ -186,12 +192,12 @@ hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, 
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const uint16_t* src, int C, const int32_t* row_token, int64_t rows, uint16_t* dst,
-                              hipStream_t st) {
+hipError_t launch_gather_rows(const uint16_t* src, int C, const int32_t* row_token, const int32_t* n_valid,
+                              int64_t rows, uint16_t* dst, hipStream_t st) {
   const int64_t n = rows * (C / 8);
   const int blocks = (int)std::min<int64_t>((n + 255) / 256, 65536);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, st, src, C, row_token, rows, dst);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, st, src, C, row_token, n_valid, rows, dst);
   return hipGetLastError();
 }
 

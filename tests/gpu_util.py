@@ -164,3 +164,43 @@ def relerr(a, b) -> float:
 
 def bf16_dev_to_f64(t: torch.Tensor) -> np.ndarray:
     return oracle.bf16_bits_to_f64(u16(t))
+
+
+def grouped_tile_kinds(offsets: np.ndarray, BM: int = 256, ntl_list=(20, 8)):
+    """Per permuted row: the height class of the grouped products' M tile that
+    holds it (1..4 quarters of BM: an expert's tail tile of at most BM/4, BM/2,
+    3BM/4 rows runs a shorter tile) and, for each product with ntl column tiles,
+    whether any of that M tile's tiles lies in the last eighth of an XCD's range
+    (the tiles handed out through the per-XCD counters).
+
+    The order is the one the grouped launch uses: an expert's tiles are
+    contiguous, its first M tile f, tile t = f * ntl + nt * ne + i for local M
+    tile i of ne and column tile nt; the valid tiles are split over 8 XCDs in
+    equal contiguous ranges, and each range's last size // 8 tiles are claimed."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    counts = np.diff(offsets)
+    ne = (counts + BM - 1) // BM
+    first = np.concatenate([[0], np.cumsum(ne)[:-1]])
+    n_mtiles = int(ne.sum())
+    rows = int(offsets[-1])
+    hclass = np.zeros(rows, dtype=np.int8)
+    claimed = {ntl: np.zeros(rows, dtype=bool) for ntl in ntl_list}
+    ranges = {}
+    for ntl in ntl_list:
+        valid = n_mtiles * ntl
+        q, r = divmod(valid, 8)
+        rr = []
+        for x in range(8):
+            start = x * q + min(x, r)
+            size = q + (1 if x < r else 0)
+            rr.append((start + size - size // 8, start + size))
+        ranges[ntl] = rr
+    for e in np.nonzero(counts)[0]:
+        for i in range(int(ne[e])):
+            a = int(offsets[e]) + i * BM
+            b = min(a + BM, int(offsets[e + 1]))
+            hclass[a:b] = (b - a + BM // 4 - 1) // (BM // 4)
+            for ntl in ntl_list:
+                ts = int(first[e]) * ntl + np.arange(ntl) * int(ne[e]) + i
+                claimed[ntl][a:b] = any(((ts >= lo) & (ts < hi)).any() for lo, hi in ranges[ntl])
+    return hclass, claimed

@@ -430,10 +430,28 @@ def pin_mirror_grid(O):
     assert 0.45 < np.mean(res["h"] == 0) < 0.55
 
 
+def pin_fp32_mode(O):
+    """The float32 timing mode runs the same steps at single precision: on tiny
+    (no token near a tie) it routes exactly as the pinned float64 mode and its
+    output agrees with it to the bf16 rounding of the stored tensors."""
+    c = case("tiny")
+    cfg = c["cfg"]
+    up, down = c["up"], c["down"]
+    res = {dt: O.forward(c["x"], c["wr"], c["b"], c["fc1"], c["fc2"], c["su"], c["sd"],
+                         lambda e: (up[e], down[e]), cfg.K, cfg.routed_scaling, dtype=dt)
+           for dt in (np.float64, np.float32)}
+    a, b = res[np.float64], res[np.float32]
+    assert np.all(a["gap"] > 1e-4)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.max(np.abs(a["gate"] - b["gate"]) / a["gate"]) < 1e-5
+    assert relerr(b["out"], a["out"]) < 1e-2
+    assert b["out"].dtype == np.float32
+
+
 ALL_PINS = [
     pin_group_bruteforce, pin_group_all_admitted_is_plain, pin_group_confinement, pin_group_tie,
     pin_bf16_conversions, pin_route_bruteforce, pin_route_bias_zero, pin_route_forced_and_gates,
     pin_route_invariants, pin_route_ties, pin_permute_bruteforce, pin_dense_masked,
     pin_dense_e1k1, pin_identity_expert, pin_zero_routed_path, pin_scale_linearity,
-    pin_token_equivariance_and_subset, pin_expert_relabel, pin_mirror_grid,
+    pin_token_equivariance_and_subset, pin_expert_relabel, pin_mirror_grid, pin_fp32_mode,
 ]

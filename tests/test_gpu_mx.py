@@ -122,7 +122,7 @@ class _OracleExperts:
 
     def prefetch(self, experts):
         todo = [int(e) for e in experts if int(e) not in self.cache]
-        with ThreadPoolExecutor(8) as pool:
+        with ThreadPoolExecutor(16) as pool:
             for e, r in zip(todo, pool.map(self._one, todo)):
                 self.cache[e] = r
         log(f"[oracle] quantised {len(todo)} experts")
@@ -181,17 +181,20 @@ def test_forward_mx_tiny(over, fmt):
     assert torch.equal(ref_out, out)
 
 
-@pytest.mark.timeout(400)
+@pytest.mark.slow
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("name", ["ultra_decode1", "ultra_decode64"])
 def test_forward_mx_ultra(name, fmt):
+    """Every token of the batch; the codes and scales of every expert they use
+    are checked bit for bit against the oracle's quantiser (about 480 experts at
+    64 tokens)."""
     d = device_inputs(name)
     cfg = d["cfg"]
     mx = _quantize_experts(d, name, fmt)
     out, idx, gate, gap = _run_mx(d, mx)
     check_routing(idx, gate, gap, oracle_route(d), label=f"{name} mx")
-    # the last token (the ragged end of the batch); its experts' codes are checked bit for bit
-    _compare(d, out, idx, np.array([cfg.T - 1]), _OracleExperts(d, mx, fmt), f"{name} {fmt}")
+    _compare(d, out, idx, np.arange(cfg.T), _OracleExperts(d, mx, fmt), f"{name} {fmt}")
 
 
 def test_forward_mx_rejects_many_tokens():

@@ -330,3 +330,47 @@ def test_identity_experts():
     out, _, _ = run_forward(d)
     assert torch.equal(out[:, :L], 5.0 * d["x"][:, :L])
     assert torch.all(out[:, L:] == 0)
+
+
+def test_permute_skips_out_of_range_entries():
+    """Entries outside [0, E) are skipped: their slot_row is -1, the valid rows
+    are [0, off[E]) and dst holds zero rows past them (nothing is read there)."""
+    T, E, K = 300, 16, 4
+    rng = np.random.default_rng(8)
+    idx = np.sort(np.argsort(rng.random((T, E)), axis=1)[:, :K], axis=1).astype(np.int32)
+    bad = rng.random((T, K)) < 0.2
+    idx[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, E + 3)
+    src = torch.randn(T, 40, device="cuda").to(torch.bfloat16)
+    tidx = torch.from_numpy(idx).cuda()
+    log(f"[permute] {int(bad.sum())} of {T * K} entries out of range")
+    off, rt, sr, dst = M.permute(tidx, E, src)
+    torch.cuda.synchronize()
+    off, rt, sr = off.cpu().numpy(), rt.cpu().numpy(), sr.cpu().numpy()
+    nv = int((~bad).sum())
+    assert off[E] == nv
+    assert np.all(sr[bad] == -1)
+    # the valid slots: the stable order of the oracle over the kept (token, expert) pairs
+    t_of = np.repeat(np.arange(T), K)[~bad.reshape(-1)]
+    e_of = idx.reshape(-1)[~bad.reshape(-1)]
+    order = np.lexsort((t_of, e_of))
+    assert np.array_equal(rt[:nv], t_of[order])
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(e_of, minlength=E))]))
+    assert np.array_equal(np.sort(sr[~bad]), np.arange(nv))
+    assert torch.equal(dst[:nv], src[torch.as_tensor(rt[:nv], device="cuda").long()])
+    assert torch.all(dst[nv:] == 0)
+
+
+def test_forward_latent_rows_past_2_gib():
+    """z [T, L] of 2.4 GB: the expert up product gathers latent rows past 2 GiB
+    through 32-bit buffer offsets (they must read the data, not zeros)."""
+    d = device_inputs("tiny", T=600000, H=64, L=2048, E=4, I=64, K=1, Is=64)
+    cfg = d["cfg"]
+    assert 2 * cfg.T * cfg.L > (1 << 31)
+    out, ws, lay = run_forward(d)
+    tokens = np.array([0, 524287, 524288, 540000, cfg.T - 1])
+    idx = ws_view(ws, lay, "idx", torch.int32, (cfg.T, cfg.K)).cpu().numpy()
+    _compare_tokens(d, out, ws, lay, tokens, idx, "latent rows past 2 GiB")
+    # the h rows of the last tokens are not all zero (a range miss reads zeros)
+    sr = ws_view(ws, lay, "slot_row", torch.int32, (cfg.T, cfg.K)).cpu().numpy()
+    h = ws_view(ws, lay, "h", torch.bfloat16, (cfg.T * cfg.K, cfg.I))
+    assert torch.count_nonzero(h[torch.as_tensor(sr[-1000:, 0].astype(np.int64), device="cuda")]) > 0

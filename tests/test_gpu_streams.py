@@ -1,8 +1,6 @@
-"""Few-token forwards run part of their work on a second stream of the
-library's, with fork and join events of their own. Forwards issued at the same
-time from two host threads, each on its own stream and workspace, must each give
-exactly their single-threaded output (with shared events one could wait on the
-other's records and read an input before it is written)."""
+"""The library keeps no state between calls and creates no stream or event:
+forwards issued at the same time from two host threads, each on its own stream
+and workspace, must each give exactly their single-threaded output."""
 import threading
 
 import pytest

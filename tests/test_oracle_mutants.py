@@ -33,9 +33,9 @@ MUTANTS = {
     "group_gap_ignored": ("gap[t] = min(egap, ggap)", "gap[t] = egap"),
     "relu_not_squared": ("return r * r", "return r"),
     "no_activation": ("r = np.maximum(a, 0.0)\n    return r * r", "return a"),
-    "shared_dropped": ("+ hs @ bf16_bits_to_f64(w_sh_down_bits).T)", ")"),
-    "shared_not_squared": ("hs = rnd(_relu2(x @ bf16_bits_to_f64(w_sh_up_bits).T))",
-                           "hs = rnd(np.maximum(x @ bf16_bits_to_f64(w_sh_up_bits).T, 0))"),
+    "shared_dropped": ("+ hs @ dec(w_sh_down_bits).T)", ")"),
+    "shared_not_squared": ("hs = rnd(_relu2(x @ dec(w_sh_up_bits).T))",
+                           "hs = rnd(np.maximum(x @ dec(w_sh_up_bits).T, 0))"),
     "combine_first_slot_only": ("y[p.slot_row[:, j]]", "y[p.slot_row[:, 0]]"),
     "gate_squared": ("gate64[:, j:j + 1] * y", "gate64[:, j:j + 1] ** 2 * y"),
     "gate_dropped_in_combine": ("gate64[:, j:j + 1] * y", "y"),
