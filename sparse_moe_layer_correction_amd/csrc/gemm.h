@@ -62,6 +62,8 @@ struct GemmProblem {
   int mtiles;                // M tiles in the grid (an upper bound in grouped mode)
   int ntiles;                // ceil(N / BN)
   int group_m;               // M tiles per raster group
+  int a_records;             // range of the A buffer resources: kRsrc2G, or kRsrc4G when the
+                             //   A rows' byte offsets reach 2 GiB (gathered rows of a large z)
 };
 
 struct GemmLaunch {
@@ -116,13 +118,17 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2_t));
 }
 
-// Buffer resource over [base, base + 2^32 - 1): raw (stride 0) descriptor, word 3
-// as the gfx9 family expects for untyped loads. A raw buffer access is in range
-// while its byte offset is below num_records, so -1 (0xFFFFFFFF) admits every
-// 32-bit offset but the last; num_records 0 makes every lane out of range: the
-// load then touches no memory (buffer range checking returns zeros).
-constexpr int kRsrcAll = -1;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_records = kRsrcAll) {
+// Buffer resource over [base, base + num_records): raw (stride 0) descriptor,
+// word 3 as the gfx9 family expects for untyped loads. A raw buffer access is
+// in range while its byte offset is below num_records; num_records 0 makes
+// every lane out of range: the load then touches no memory (buffer range
+// checking returns zeros). kRsrc2G covers every offset below 2 GiB; kRsrc4G
+// (0xFFFFFFFF) every 32-bit offset but the last, for operands whose rows lie
+// past 2 GiB from their base -- measured 17 % slower on every product of the
+// Ultra prefill when used for all loads, so it is taken only where needed.
+constexpr int kRsrc2G = 0x7FFFFFFF;
+constexpr int kRsrc4G = -1;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_records = kRsrc2G) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, 0x00020000);
 }
 
@@ -319,8 +325,8 @@ gemm_bf16_kernel(const GemmLaunch L) {
         point(seg);
       }
       const int so = (kt - seg_k0) * BK * 2;
-      const int nrec = live ? kRsrcAll : 0;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, nrec), rb = make_rsrc(bbase, nrec);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, live ? P.a_records : 0),
+                                   rb = make_rsrc(bbase, live ? kRsrc2G : 0);
       // (the explicit casts of the lane offsets matter: without them the host
       // pass silently drops this kernel's launch stub)
       u32x4* a = stA(st);

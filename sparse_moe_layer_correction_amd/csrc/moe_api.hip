@@ -179,6 +179,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 GemmProblem dense_problem(int cfg, int M, int N, int Nb, void* C, int64_t ldc, int epi) {
   GemmProblem p{};
   const TileShape ts = tile_shape(cfg);
+  p.a_records = kRsrc2G;
   p.M = M;
   p.N = N;
   p.Nb = Nb;
@@ -535,6 +536,8 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     p.N = d.I;
     p.Nb = d.I;
     p.gather = row_token;
+    // gathered z rows are addressed from z's base: past 2 GiB the full 32-bit range
+    p.a_records = T * L * 2 > (int64_t)kRsrc2G ? kRsrc4G : kRsrc2G;
     p.tile_info = ps.tile_info;
     p.n_mtiles = ps.n_mtiles;
     p.offsets = offsets;
@@ -565,6 +568,7 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     GemmProblem& p = G.p[0];
     p.N = d.L;
     p.Nb = d.L;
+    p.a_records = kRsrc2G;
     p.tile_info = ps.tile_info;
     p.n_mtiles = ps.n_mtiles;
     p.offsets = offsets;
