@@ -91,7 +91,8 @@ enum moe_status {
   MOE_ERR_UNSUPPORTED = -2,  /* H, L, I or Is not a multiple of 64; E > 1024; K > 64;
                                 T*K >= 2^31; 2*T*L >= 2^32 */
   MOE_ERR_WORKSPACE = -3,    /* workspace null, too small or not 256-byte aligned */
-  MOE_ERR_HIP = -4           /* a HIP launch failed */
+  MOE_ERR_HIP = -4,          /* a HIP launch failed */
+  MOE_ERR_TOO_LARGE = -5     /* moe_forward_noalloc: the forward needs more than its static scratch */
 };
 
 /* Byte offsets, inside the moe_forward workspace, of the intermediate tensors
@@ -287,6 +288,29 @@ int moe_block_forward(const moe_dims* dims, const moe_weights* w, const moe_expe
  * fp32, updated in place. MOE_ERR_INVALID for null pointers, E <= 0 or a
  * non-finite eta. Asynchronous on `stream`. */
 int moe_bias_update(const int32_t* offsets, int32_t E, float eta, float* corr_bias, hipStream_t stream);
+
+/* ---- allocation-free forward ------------------------------------------ */
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: moe_forward
+ * with its workspace taken from a scratch array of the library's own instead of
+ * the caller's. The array is a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * (128 MiB); each GPU the library is loaded on holds its own copy until the
+ * process ends. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks the array's
+ * address up once (hipGetSymbolAddress) and keeps it for that device.
+ *   dims, w, x, out, stream: as for moe_forward (same results, bit for bit).
+ * Returns MOE_ERR_TOO_LARGE, before any HIP call, when moe_workspace_bytes(dims)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES (the Ultra-shape layer fits up to 64 tokens
+ * at a time; larger batches take moe_forward with a caller workspace), the
+ * errors of moe_forward otherwise, and MOE_ERR_HIP if the array's address
+ * cannot be looked up. Every call on one GPU uses that GPU's one array, which
+ * keeps the last call's intermediates: calls that overlap in time on one GPU
+ * (two streams, two host threads) race and must be ordered by the caller.
+ * Nothing in the array needs to start at zero. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int moe_forward_noalloc(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out,
+                        hipStream_t stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(int status);

@@ -24,7 +24,7 @@ from typing import Dict, Optional
 __all__ = [
     "MoEError", "MoEDims", "load_library", "library_path", "EXPORTS", "route", "permute", "forward",
     "workspace_bytes", "route_workspace_bytes", "permute_workspace_bytes", "workspace_layout",
-    "LatentMoE", "PhaseEvents", "forward_profiled", "PHASES",
+    "LatentMoE", "PhaseEvents", "forward_profiled", "PHASES", "forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,11 @@ EXPORTS = (
     "moe_workspace_bytes", "moe_workspace_layout", "moe_forward", "moe_forward_profiled", "moe_status_string",
     "moe_abi_version", "moe_quantize_mxfp8", "moe_forward_mx", "moe_forward_mx_profiled",
     "moe_rmsnorm", "moe_block_workspace_bytes", "moe_block_forward", "moe_bias_update", "moe_quantize_mxfp4",
+    "moe_forward_noalloc",
 )
+
+# MOE_NOALLOC_SCRATCH_BYTES of include/moe_api.h
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 # enum moe_phase of include/moe_api.h
 PHASES = ("router_split", "router_gemm", "topk", "permute", "fc1_shared_up", "expert_up", "expert_down",
@@ -131,6 +135,7 @@ def load_library(path: Optional[str] = None):
         "moe_block_forward": (i32, [dims_p, ctypes.POINTER(_Weights), ctypes.POINTER(_ExpertsMx), vp, ctypes.c_float,
                                     vp, vp, vp, sz, vp]),
         "moe_bias_update": (i32, [vp, ctypes.c_int32, ctypes.c_float, vp, vp]),
+        "moe_forward_noalloc": (i32, [dims_p, ctypes.POINTER(_Weights), vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -421,6 +426,25 @@ def forward(x, weights: Dict, K: int, routed_scaling: float = 5.0, *, out=None, 
     w = _workspace(nbytes, dev, ws)
     _check(lib.moe_forward(ctypes.byref(d), ctypes.byref(wstruct), _ptr(x), _ptr(out), _ptr(w),
                            w.numel() * w.element_size(), _stream(stream)))
+    return out
+
+
+def forward_noalloc(x, weights: Dict, K: int, routed_scaling: float = 5.0, *, out=None, stream=None,
+                    n_group: int = 1, topk_group: int = 1):
+    """moe_forward_noalloc: the forward with the library's static device scratch as
+    its workspace (no allocation by the library; ``out`` is allocated here only
+    when not given). Raises for batches whose workspace exceeds that scratch."""
+    torch = _torch()
+    dims = dims_from(x, weights, K, routed_scaling, n_group, topk_group)
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (dims.T, dims.H), dev)
+    wstruct = _weight_struct(dims, weights, dev)
+    if out is None:
+        out = torch.empty(dims.T, dims.H, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (dims.T, dims.H), dev)
+    d = dims.c()
+    _check(load_library().moe_forward_noalloc(ctypes.byref(d), ctypes.byref(wstruct), _ptr(x), _ptr(out),
+                                              _stream(stream)))
     return out
 
 

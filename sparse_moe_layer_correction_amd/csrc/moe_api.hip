@@ -5,6 +5,8 @@
 
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -329,7 +331,7 @@ PermuteScratch permute_scratch(const Layout& l, void* ws, size_t origin) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 104; }
+int moe_abi_version(void) { return 105; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -341,6 +343,8 @@ const char* moe_status_string(int status) {
              "2*T*L < 2^32; n_group <= 64)";
     case MOE_ERR_WORKSPACE: return "workspace null, too small or not 256-byte aligned";
     case MOE_ERR_HIP: return "HIP launch error";
+    case MOE_ERR_TOO_LARGE:
+      return "the forward needs more workspace than the allocation-free entry point's static scratch (128 MiB)";
     default: return "unknown status";
   }
 }
@@ -687,6 +691,47 @@ int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int32_t cols, uint8_t*
   if (src == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID;
   if (((uintptr_t)src | (uintptr_t)codes) & 15) return MOE_ERR_INVALID;
   return hip_status(launch_mxfp8_quantize(src, rows * (cols / 32), codes, scales, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free forward: a static device array (one copy per
+// GPU, held until the process ends). In host code its name is only a stand-in;
+// kernels take the device address looked up below.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of the current device's copy of `scratch`, looked up on
+// the first call on each device and kept; nullptr if the lookup fails.
+void* scratch_for_current_device() {
+  static std::mutex mu;
+  static void* per_dev[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    per_dev[dev] = p;
+  }
+  return per_dev[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_dims* dims, const moe_weights* w, const uint16_t* x, uint16_t* out,
+                        hipStream_t stream) {
+  int st;
+  if (!dims_ok(dims, &st)) return st;
+  if (make_layout(*dims).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ws = scratch_for_current_device();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  return forward_impl(dims, w, x, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, Marks{nullptr, stream});
 }
 
 }  // extern "C"

@@ -40,11 +40,11 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.moe_abi_version() == 104
+    assert lib.moe_abi_version() == 105
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.moe_status_string(code), bytes)
     assert lib.moe_status_string(-3).startswith(b"workspace")
 
@@ -242,3 +242,18 @@ def test_latent_rows_up_to_4_gib_accepted(lib):
     assert lib.moe_workspace_bytes(_d(d)) > 2 * d.T * d.L
     d = M.MoEDims(1 << 20, 64, 2048, 4, 64, 1, 64, 5.0)
     assert lib.moe_workspace_bytes(_d(d)) == 0
+
+
+def test_noalloc_rejects_batches_beyond_its_scratch(lib):
+    """The allocation-free forward refuses, before any HIP call, a batch whose
+    workspace exceeds its static scratch (the Ultra prefill) and names the reason."""
+    w = M._Weights()
+    assert lib.moe_workspace_bytes(_d(ULTRA)) > M.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(_d(ULTRA), ctypes.byref(w), None, None, None) == -5
+    assert b"static scratch" in lib.moe_status_string(-5)
+    # the Ultra-shape decode batch fits
+    dec = M.MoEDims(64, 8192, 2048, 512, 5120, 22, 10240, 5.0)
+    assert 0 < lib.moe_workspace_bytes(_d(dec)) <= M.NOALLOC_SCRATCH_BYTES
+    # invalid dims are still MOE_ERR_INVALID
+    bad = M.MoEDims(0, 8192, 2048, 512, 5120, 22, 10240, 5.0)
+    assert lib.moe_forward_noalloc(_d(bad), ctypes.byref(w), None, None, None) == -1
