@@ -289,6 +289,9 @@ gemm_bf16_kernel(const GemmLaunch L) {
       bcol[i] = swz_slot(r, p % CPR) * 16;
     }
 
+    // the A buffer range, read once: a kernel-argument load inside the loop
+    // would be followed by a wait for all scalar and LDS reads in flight
+    const int arec = __builtin_amdgcn_readfirstlane(P.a_records);
     // K segments, walked by the load issue in increasing k-tile order.
     int nk = 0;
     for (int s = 0; s < P.nseg; ++s) nk += P.seg[s].K / BK;
@@ -325,7 +328,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
         point(seg);
       }
       const int so = (kt - seg_k0) * BK * 2;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, live ? P.a_records : 0),
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, live ? arec : 0),
                                    rb = make_rsrc(bbase, live ? kRsrc2G : 0);
       // (the explicit casts of the lane offsets matter: without them the host
       // pass silently drops this kernel's launch stub)
