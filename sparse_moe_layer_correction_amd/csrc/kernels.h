@@ -56,6 +56,11 @@ struct SkinnyProblem {
 // the weight operand of a skinny product: bf16, MXFP8 or MXFP4 codes and scales, or fp32
 enum SkinnyBMode : int { kSkinnyBf16 = 0, kSkinnyMx = 1, kSkinnyF32 = 2, kSkinnyMx4 = 3 };
 hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st);
+// dense bf16 products of 1..16 rows, K split over the waves of a workgroup and
+// reduced in LDS (no partials, no second pass); P1: an optional second problem
+// in the same launch
+hipError_t launch_skinny_wgk(const SkinnyProblem& P0, const SkinnyProblem* P1, hipStream_t st);
+constexpr int kWgkMaxRows = 16;
 hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t nblocks, uint8_t* codes, uint8_t* scales,
                                  hipStream_t st);
 hipError_t launch_mxfp4_quantize(const uint16_t* src, int64_t nblocks, uint8_t* codes, uint8_t* scales,

@@ -313,8 +313,9 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (mk.mark(MOE_PHASE_TOPK) != hipSuccess) return MOE_ERR_HIP;
-  e = launch_topk(logits, logits2, ldl, nparts, d.E, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d), topk_groups_of(d), idx, gate,
-                  gap, st);
+  // (stacked weight parts lie E columns apart in a logit row)
+  e = launch_topk(logits, logits2, ldl, nparts, d.E, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d),
+                  topk_groups_of(d), idx, gate, gap, st);
   return hip_status(e);
 }
 
@@ -505,10 +506,15 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     if (mk.mark(MOE_PHASE_FC1_SHARED_UP) != hipSuccess) return MOE_ERR_HIP;
     SkinnyProblem P = skinny_dense(d.T, d.L, d.L, z, L, EPI_BF16, d.H, partial);
     add_seg(P, x, H, w->w_fc1, H, d.H);
-    if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
     SkinnyProblem Q = skinny_dense(d.T, d.Is, d.Is, hs, Is, EPI_RELU2_BF16, d.H, partial);
     add_seg(Q, x, H, w->w_sh_up, H, d.H);
-    if (launch_skinny(Q, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (d.T <= kWgkMaxRows) {
+      // both products in one launch, K split inside each workgroup
+      if (launch_skinny_wgk(P, &Q, stream) != hipSuccess) return MOE_ERR_HIP;
+    } else {
+      if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
+      if (launch_skinny(Q, stream) != hipSuccess) return MOE_ERR_HIP;
+    }
   } else {
     const int cfg = choose_dense_cfg(d.T, std::min(d.L, d.Is));
     GemmLaunch G{};
@@ -601,7 +607,8 @@ int forward_impl(const moe_dims* dims, const moe_weights* w, const uint16_t* x, 
     P.ldr = H;
     add_seg(P, y_lat, L, w->w_fc2, L, d.L);
     add_seg(P, hs, Is, w->w_sh_down, Is, d.Is);
-    if (launch_skinny(P, stream) != hipSuccess) return MOE_ERR_HIP;
+    if ((d.T <= kWgkMaxRows ? launch_skinny_wgk(P, nullptr, stream) : launch_skinny(P, stream)) != hipSuccess)
+      return MOE_ERR_HIP;
   } else {
     const int cfg = choose_dense_cfg(d.T, d.H);
     GemmLaunch G{};

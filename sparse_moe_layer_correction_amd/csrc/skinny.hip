@@ -132,7 +132,8 @@ int skinny_slabs_per_wave(const SkinnyProblem& P) {
 template <int MT, int NS, int UNROLL, int BMODE>
 __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first, int rows, int row0,
                                             const int32_t* gather, int64_t b_base, int k_begin, int k_end,
-                                            int out_row0, float* partial, int lane, int epi) {
+                                            int out_row0, float* partial, int lane, int epi,
+                                            f32x4v* acc_out = nullptr) {
   // rows of the MT m-tiles this lane loads (clamped: padding lanes re-read a valid row)
   int64_t arow[MT];
 #pragma unroll
@@ -309,6 +310,13 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProblem& P, int n_first,
     seg_k0 += S.K;
   }
 
+  if (acc_out != nullptr) {                   // the caller reduces and stores
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc_out[j * MT + t] = acc[j][t];
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int n = n_first + j * 16 + (lane >> 4) * 4;
@@ -650,6 +658,70 @@ __global__ void __launch_bounds__(256) skinny_kernel(const SkinnyProblem P) {
       skinny_tile<4, NSB, unroll_steps(4, NSB, BMODE), BMODE>(P, n_first, rr, row0 + r0, P.gather, b_base, k_begin,
                                                              k_end, row0 + r0, partial, lane, epi);
   }
+}
+
+// Dense products of 1..16 rows with K split inside the workgroup: the KW waves
+// of a workgroup take KW consecutive k ranges of one 16-column slab, leave their
+// fp32 sums in LDS, and wave 0 adds them in wave order and applies the
+// epilogue. The same fixed order on every call, no partials in global memory
+// and no reduction launch (the split over workgroups needed a second pass).
+// Up to two problems per launch (fc1 and the shared expert's up product read
+// the same rows): workgroup b < slabs0 takes slab b of the first.
+struct SkinnyPair {
+  SkinnyProblem p[2];
+  int slabs0;                // slabs of p[0]; the workgroups after them take p[1]
+};
+
+template <int KW>
+__global__ void __launch_bounds__(64 * KW) skinny_wgk_kernel(const SkinnyPair L) {
+  __shared__ f32x4v red[KW][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int slab = blockIdx.x;
+  const int pi = slab >= L.slabs0 ? 1 : 0;
+  slab -= pi * L.slabs0;
+  const SkinnyProblem& P = L.p[pi];
+  const int n_first = slab * 16;
+  int ktot = 0;
+  for (int s = 0; s < P.nseg; ++s) ktot += P.seg[s].K;
+  const int ksteps = ktot / 64;
+  const int k_begin = ksteps * w / KW * 64, k_end = ksteps * (w + 1) / KW * 64;
+  f32x4v acc;
+  skinny_tile<1, 1, unroll_steps(1, 1, kSkinnyBf16), kSkinnyBf16>(P, n_first, P.M, 0, nullptr, 0, k_begin, k_end, 0,
+                                                                   nullptr, lane, P.epi, &acc);
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+  f32x4v v = red[0][lane];
+#pragma unroll
+  for (int i = 1; i < KW; ++i) v += red[i][lane];
+  // lane l holds row l % 16 and columns 4 * (l / 16) + 0..3 of the slab
+  const int m = lane & 15, n = n_first + (lane >> 4) * 4;
+  if (m >= P.M || n >= P.N) return;
+  if (P.epi == EPI_F32) {
+    *reinterpret_cast<f32x4v*>(static_cast<float*>(P.C) + (int64_t)m * P.ldc + n) = v;
+    return;
+  }
+  if (P.epi == EPI_RELU2_BF16) {
+    v[0] = relu2(v[0]); v[1] = relu2(v[1]); v[2] = relu2(v[2]); v[3] = relu2(v[3]);
+  }
+  *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.C) + (int64_t)m * P.ldc + n) =
+      P.residual ? add_residual_bf16x4(v, P.residual + (int64_t)m * P.ldr + n)
+                 : u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+constexpr int kWgkWaves = 16;
+
+hipError_t launch_skinny_wgk(const SkinnyProblem& P0, const SkinnyProblem* P1, hipStream_t st) {
+  const int s0 = (P0.N + 15) / 16;
+  const int s1 = P1 ? (P1->N + 15) / 16 : 0;
+  if (s0 + s1 <= 0) return hipSuccess;
+  SkinnyPair L;
+  L.p[0] = P0;
+  L.p[1] = P1 ? *P1 : P0;
+  L.slabs0 = s0;
+  hipLaunchKernelGGL(skinny_wgk_kernel<kWgkWaves>, dim3(s0 + s1), dim3(64 * kWgkWaves), 0, st, L);
+  return hipGetLastError();
 }
 
 // out[m, n] = epi(sum_{s < ksplit} partial[s, m, n]), summed in split order.
