@@ -160,7 +160,9 @@ __device__ __forceinline__ void interleave() {
 // EPI: an Epilogue fixed at compile time, or -1 to take each problem's own.
 // OCC: waves per SIMD the register allocation is sized for (1 lets the 256x256
 // tile keep its 256 accumulators per lane in AGPRs next to 256 VGPRs).
-template <int BM, int BN, int WM, int WN, int EPI, int OCC>
+// BST: LDS stages of B: 2, or 3 for launches whose problems have one K segment
+// each (see the main loop).
+template <int BM, int BN, int WM, int WN, int EPI, int OCC, int BST = 2>
 __global__ void __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_bf16_kernel(const GemmLaunch L) {
   constexpr int BK = 64, CPR = 8;                  // k tile: 64 bf16 = 128 bytes per row
@@ -172,9 +174,12 @@ gemm_bf16_kernel(const GemmLaunch L) {
   constexpr int ACH = BM * CPR, BCH = BN * CPR;    // 16-byte chunks per stage
   static_assert(TM >= 1 && TN >= 1 && NA >= 1 && NB >= 1, "tile shape");
   static_assert(NA * NT == ACH && NB * NT == BCH, "load coverage");
-  // two stages, each its own array so that the compiler can tell the stage
-  // being filled from the one being read
-  __shared__ u32x4 sa0[ACH], sb0[BCH], sa1[ACH], sb1[BCH];
+  static_assert(BST == 2 || BST == 3, "B stages");
+  // two stages (B: BST), each its own array so that the compiler can tell the
+  // stage being filled from the one being read. With three B stages the LDS is
+  // full (2 x 32 + 3 x 32 KiB at 256x256), and the tile claim's word lives in
+  // the third B stage, which no load fills before every wave has read it.
+  __shared__ u32x4 sa0[ACH], sb0[BCH], sa1[ACH], sb1[BCH], sb2[BST == 3 ? BCH : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -204,7 +209,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
       if (j < fixed) {
         t = x * q + min(x, r) + j;
       } else {
-        __shared__ int claim;
+        int& claim = *reinterpret_cast<int*>(sb2);
         if (tid == 0) {
           int tt = -1;
           for (int d = 0; d < 8 && tt < 0; ++d) {
@@ -220,6 +225,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
         __syncthreads();
         t = __builtin_amdgcn_readfirstlane(claim);
         if (t < 0) return;
+        if constexpr (BST == 3) __syncthreads();   // every wave has read the word before loads fill sb2
       }
     } else {
       const int valid = *L.p[0].n_mtiles * ntl;
@@ -432,16 +438,135 @@ gemm_bf16_kernel(const GemmLaunch L) {
       interleave<NM, NR, N3>();
     };
 
-    issue(0, Stage<0>{});
-    issue(min(1, nk - 1), Stage<1>{});
-    MOE_WAIT_VMCNT(NAX + NB);
-    __syncthreads();
-    read(f0, Stage<0>{}, 0);
-    for (int kt = 0; kt + 1 < nk; kt += 2) {
-      step(kt, Stage<0>{});
-      step(kt + 1, Stage<1>{});
+    if constexpr (BST == 2) {
+      issue(0, Stage<0>{});
+      issue(min(1, nk - 1), Stage<1>{});
+      MOE_WAIT_VMCNT(NAX + NB);
+      __syncthreads();
+      read(f0, Stage<0>{}, 0);
+      for (int kt = 0; kt + 1 < nk; kt += 2) {
+        step(kt, Stage<0>{});
+        step(kt + 1, Stage<1>{});
+      }
+      if (nk & 1) step(nk - 1, Stage<0>{});
+    } else {
+      // Three B stages (launches whose problems have one K segment each): B tile kt+3 is loaded from the barrier
+      // of step kt on, so a B load has two steps to land instead of one (A
+      // keeps one). In the grouped products the weight panels come from HBM,
+      // and the weights of the 10-20 panels that an XCD's workgroups start on
+      // together all miss at once. A tile's stages: A kt % 2, B kt % 3.
+      auto stB3 = [&](auto st) -> u32x4* {
+        constexpr int v = decltype(st)::value;
+        if constexpr (v == 0) return sb0;
+        else if constexpr (v == 1) return sb1;
+        else return sb2;
+      };
+      auto issueA = [&](int kt, auto st, bool live) {
+        const int so = kt * BK * 2;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, live ? arec : 0);
+        u32x4* a = stA(st);
+  #pragma unroll
+        for (int i = 0; i < NAX; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)&a[(wave * NAX + i) * 64], 16, (int)ao[i], so, 0,
+                                                   0);
+      };
+      auto issueB = [&](int kt, auto st, bool live, int parts) {
+        const int so = kt * BK * 2;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase, live ? kRsrc2G : 0);
+        u32x4* b = stB3(st);
+  #pragma unroll
+        for (int i = 0; i < NB; ++i)
+          if (parts & (i < NB / 2 ? 4 : 8))
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)&b[(wave * NB + i) * 64], 16, (int)bo[i], so,
+                                                     0, 0);
+      };
+      auto read3 = [&](Frag& f, auto sa, auto sb, int ks) {
+        const u32x4* a = stA(sa);
+        const u32x4* b = stB3(sb);
+        const int ch = ks * 2 + (lane >> 5);
+  #pragma unroll
+        for (int tm = 0; tm < TMX; ++tm) {
+          const int r = wave_m * WTMX + tm * 32 + (lane & 31);
+          f.a[tm] = __builtin_bit_cast(bf16x8, a[r * CPR + swz_slot(r, ch)]);
+        }
+  #pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int r = wave_n * WTN + tn * 32 + (lane & 31);
+          f.b[tn] = __builtin_bit_cast(bf16x8, b[r * CPR + swz_slot(r, ch)]);
+        }
+      };
+      // the plan's B quarters: at the barrier of step kt (tile kt+3), or in the
+      // first / second substep of step kt+1; A is loaded whole at the barrier,
+      // so that the last NB loads issued before a barrier are one B tile's
+      static_assert(((M0 | M1) & 3) == 0, "A quarters at the barrier");
+      constexpr int NB0 = N0, NB1 = N1, NX3 = NAX + (N3 - (M3 & 1 ? QN[0] : 0) - (M3 & 2 ? QN[1] : 0));
+      // s_waitcnt vmcnt(NB) lgkmcnt(0): tile kt+1 has landed once no more than
+      // the NB loads of B tile kt+2 are in flight
+      constexpr int kWaitB = (NB & 0xF) | (0x7 << 4) | (0x0 << 8) | (((NB >> 4) & 3) << 14);
+      // (step 0 is its own copy, FIRST: B tile 2 was loaded whole before it. A
+      // run-time test there left the compiler's count of loads in flight
+      // unknown at the loop head, and it then waited for B tile kt+2 after
+      // the barrier of every sixth step.)
+      auto step3 = [&](int kt, auto sa, auto sb, auto first) {
+        constexpr int SA = decltype(sa)::value, SB = decltype(sb)::value;
+        constexpr bool FIRST = decltype(first)::value != 0;
+        read3(f1, sa, sb, 1);
+        if constexpr (M0 != 0 && !FIRST) issueB(min(kt + 2, nk - 1), Stage<(SB + 2) % 3>{}, kt + 2 < nk, M0);
+        mma(f0);
+        interleave<NM, NR, FIRST ? 0 : NB0>();
+        read3(f0, sa, sb, 2);
+        if constexpr (M1 != 0 && !FIRST) issueB(min(kt + 2, nk - 1), Stage<(SB + 2) % 3>{}, kt + 2 < nk, M1);
+        mma(f1);
+        interleave<NM, NR, FIRST ? 0 : NB1>();
+        read3(f1, sa, sb, 3);
+        mma(f0);
+        interleave<NM, NR, 0>();
+        __builtin_amdgcn_s_waitcnt(kWaitB);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        issueA(min(kt + 2, nk - 1), sa, kt + 2 < nk);
+        if constexpr ((M3 & 12) != 0) issueB(min(kt + 3, nk - 1), sb, kt + 3 < nk, M3);
+        read3(f0, Stage<1 - SA>{}, Stage<(SB + 1) % 3>{}, 0);
+        mma(f1);
+        interleave<NM, NR, NX3>();
+      };
+      issueA(0, Stage<0>{}, true);
+      issueB(0, Stage<0>{}, true, 12);
+      issueA(min(1, nk - 1), Stage<1>{}, true);
+      issueB(min(1, nk - 1), Stage<1>{}, true, 12);
+      issueB(min(2, nk - 1), Stage<2>{}, true, 12);
+      // tile 0 has landed once tile 1 and B tile 2 are all that is in flight
+      // (an explicit wait and barrier: __syncthreads would wait for every load)
+      MOE_WAIT_VMCNT(NAX + 2 * NB);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      read3(f0, Stage<0>{}, Stage<0>{}, 0);
+      step3(0, Stage<0>{}, Stage<0>{}, Stage<1>{});
+      // step kt reads A stage kt % 2 and B stage kt % 3: from kt = 1 the pattern
+      // (1,1) (0,2) (1,0) (0,1) (1,2) (0,0) repeats
+      int kt = 1;
+      for (; kt + 6 <= nk; kt += 6) {
+        step3(kt, Stage<1>{}, Stage<1>{}, Stage<0>{});
+        step3(kt + 1, Stage<0>{}, Stage<2>{}, Stage<0>{});
+        step3(kt + 2, Stage<1>{}, Stage<0>{}, Stage<0>{});
+        step3(kt + 3, Stage<0>{}, Stage<1>{}, Stage<0>{});
+        step3(kt + 4, Stage<1>{}, Stage<2>{}, Stage<0>{});
+        step3(kt + 5, Stage<0>{}, Stage<0>{}, Stage<0>{});
+      }
+      if (kt < nk) {
+        step3(kt, Stage<1>{}, Stage<1>{}, Stage<0>{});
+        if (kt + 1 < nk) {
+          step3(kt + 1, Stage<0>{}, Stage<2>{}, Stage<0>{});
+          if (kt + 2 < nk) {
+            step3(kt + 2, Stage<1>{}, Stage<0>{}, Stage<0>{});
+            if (kt + 3 < nk) {
+              step3(kt + 3, Stage<0>{}, Stage<1>{}, Stage<0>{});
+              if (kt + 4 < nk) step3(kt + 4, Stage<1>{}, Stage<2>{}, Stage<0>{});
+            }
+          }
+        }
+      }
     }
-    if (nk & 1) step(nk - 1, Stage<0>{});
     MOE_WAIT_VMCNT(0);   // no load may still be writing this workgroup's LDS when it ends
 
     // Epilogue. Lane l owns row (l & 31) of each 32x32 MFMA tile and, for
