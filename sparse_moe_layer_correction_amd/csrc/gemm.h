@@ -160,8 +160,7 @@ __device__ __forceinline__ void interleave() {
 // EPI: an Epilogue fixed at compile time, or -1 to take each problem's own.
 // OCC: waves per SIMD the register allocation is sized for (1 lets the 256x256
 // tile keep its 256 accumulators per lane in AGPRs next to 256 VGPRs).
-// BST: LDS stages of B: 2, or 3 for launches whose problems have one K segment
-// each (see the main loop).
+// BST: LDS stages of B, 2 or 3 (3 for the 256x256 tiles: see the main loop).
 template <int BM, int BN, int WM, int WN, int EPI, int OCC, int BST = 2>
 __global__ void __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_bf16_kernel(const GemmLaunch L) {
@@ -450,7 +449,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
       }
       if (nk & 1) step(nk - 1, Stage<0>{});
     } else {
-      // Three B stages (launches whose problems have one K segment each): B tile kt+3 is loaded from the barrier
+      // Three B stages: B tile kt+3 is loaded from the barrier
       // of step kt on, so a B load has two steps to land instead of one (A
       // keeps one). In the grouped products the weight panels come from HBM,
       // and the weights of the 10-20 panels that an XCD's workgroups start on
@@ -461,8 +460,24 @@ gemm_bf16_kernel(const GemmLaunch L) {
         else if constexpr (v == 1) return sb1;
         else return sb2;
       };
+      // A and B walk the K segments apart (B one tile ahead): each has its own
+      // segment position, and a segment change re-points only its operand. The
+      // grouped products (fixed epilogue) have one segment: no walk.
+      int sega = 0, sega_k0 = 0, sega_end = P.seg[0].K / BK;
+      int segb = 0, segb_k0 = 0, segb_end = sega_end;
       auto issueA = [&](int kt, auto st, bool live) {
-        const int so = kt * BK * 2;
+        if constexpr (EPI < 0) {
+          while (kt >= sega_end) {     // uniform; at most nseg-1 times in the whole loop
+            sega_k0 = sega_end;
+            ++sega;
+            sega_end += P.seg[sega].K / BK;
+            const KSeg& S = P.seg[sega];
+            abase = P.gather ? S.A : S.A + (int64_t)m0 * S.lda;
+  #pragma unroll
+            for (int i = 0; i < NAX; ++i) ao[i] = (uint32_t)((int64_t)arow[i] * S.lda * 2 + acol[i]);
+          }
+        }
+        const int so = (kt - sega_k0) * BK * 2;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, live ? arec : 0);
         u32x4* a = stA(st);
   #pragma unroll
@@ -471,7 +486,18 @@ gemm_bf16_kernel(const GemmLaunch L) {
                                                    0);
       };
       auto issueB = [&](int kt, auto st, bool live, int parts) {
-        const int so = kt * BK * 2;
+        if constexpr (EPI < 0) {
+          while (kt >= segb_end) {
+            segb_k0 = segb_end;
+            ++segb;
+            segb_end += P.seg[segb].K / BK;
+            const KSeg& S = P.seg[segb];
+            bbase = S.B + b_base + (int64_t)n0 * S.ldb;
+  #pragma unroll
+            for (int i = 0; i < NB; ++i) bo[i] = (uint32_t)((int64_t)brow[i] * S.ldb * 2 + bcol[i]);
+          }
+        }
+        const int so = (kt - segb_k0) * BK * 2;
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase, live ? kRsrc2G : 0);
         u32x4* b = stB3(st);
   #pragma unroll
