@@ -400,7 +400,11 @@ gemm_bf16_kernel(const GemmLaunch L) {
     // burst that put them out of step (the barrier then waits for the slowest):
     // spreading the B half over the next tile's first substeps took 3-6 % off
     // every product on the Ultra prefill, the best split differing by product.
-    constexpr int PLAN = EPI == EPI_RELU2_BF16 ? 3300 : 3301;
+    // With three B stages (a sweep of 6 plans over the Ultra prefill, Nano and
+    // Super): both B halves in the second substep for expert up and the dense
+    // products (1-2 % ahead of the two-stage plans at Nano and Super, equal at
+    // Ultra), the two-stage plan for expert down; all at the barrier 4-10 % slower.
+    constexpr int PLAN = EPI == EPI_BF16 ? 3301 : 3311;
     constexpr int QD[4] = {PLAN / 1000, PLAN / 100 % 10, PLAN / 10 % 10, PLAN % 10};
     constexpr int QN[4] = {NAX / 2, NAX - NAX / 2, NB / 2, NB - NB / 2};
     constexpr int M0 = (QD[0] == 0) | (QD[1] == 0) << 1 | (QD[2] == 0) << 2 | (QD[3] == 0) << 3;
