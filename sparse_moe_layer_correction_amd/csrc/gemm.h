@@ -232,7 +232,8 @@ gemm_bf16_kernel(const GemmLaunch L) {
       t = xcd_remap(blockIdx.x, valid);
     }
     // expert by expert: the tiles of one expert are contiguous in the order,
-    // M fastest, so the M tiles that share a weight panel run side by side
+    // in rasters of group_m M tiles (M fastest in a raster), so the M tiles that
+    // share a weight panel run side by side
     // (an expert's ne M tiles times ntl N tiles are contiguous in t, starting at
     // its first M tile f times ntl, so t / ntl lands on one of the expert's own
     // M tiles, whose entry holds e, f and the expert's rows; its tiles start at
@@ -242,9 +243,12 @@ gemm_bf16_kernel(const GemmLaunch L) {
     const int e = info.x, f = info.y, o0 = info.z, o1 = info.w;
     const int ne = (o1 - o0 + BM - 1) / BM;
     const int local = t - f * ntl;
-    m0 = o0 + (local % ne) * BM;
+    // inside an expert, rasters of group_m M tiles (M fastest in a group)
+    int mt, nt;
+    tile_order(local, ne, ntl, L.p[0].group_m, mt, nt);
+    m0 = o0 + mt * BM;
     mend = o1;
-    n0 = (local / ne) * BN;
+    n0 = nt * BN;
     b_base = (int64_t)e * L.p[0].b_estride;
   } else {
     int bid = xcd_remap(blockIdx.x, gridDim.x);
