@@ -235,7 +235,11 @@ def _compare_tokens(d, out, ws, lay, tokens, idx_gpu, label):
                                        # 32 experts x about 256 rows x 4 column tiles: 128 grouped
                                        # tiles, so each XCD's last eighth is claimed through its
                                        # counter (every output and intermediate row checked)
-                                       ("tiny", dict(T=2048, H=512, L=256, E=32, I=1024, Is=512, K=4))])
+                                       ("tiny", dict(T=2048, H=512, L=256, E=32, I=1024, Is=512, K=4)),
+                                       # 2 experts of about 10 M tiles: expert down's rasters of 8 M
+                                       # tiles and a partial one; k tiles 5 (up) and 6 (down), the
+                                       # main loop's last two remainder lengths after its 6-step unroll
+                                       ("tiny", dict(T=5000, H=64, L=320, E=2, I=384, Is=64, K=1))])
 def test_forward_tiny_full(name, over):
     d = device_inputs(name, **over)
     cfg = d["cfg"]
@@ -277,6 +281,9 @@ def _sample(T, n, seed):
     ("ultra_decode1", {}, 1),
     ("ultra_decode64", {}, 3),
     ("ultra_prefill", {}, 3),
+    # 256x256 dense tiles (one wave of 256 in each dense product): fc1 + shared up
+    # over 128 k tiles, fc2 + shared down over two segments of 5 and 120 k tiles
+    ("tiny", dict(T=2048, H=8192, L=320, E=8, I=384, Is=7680, K=2), 6),
 ])
 def test_forward_sampled(name, over, n):
     d = device_inputs(name, **over)
