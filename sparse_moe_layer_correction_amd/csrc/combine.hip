@@ -25,8 +25,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
   const int my_row = lane < K ? slot_row[(int64_t)t * K + lane] : 0;
   const float my_g = lane < K ? gate[(int64_t)t * K + lane] : 0.f;
 
-  // every lane runs every iteration (the shuffles need all lanes); only the
-  // loads and the store are guarded when L is not a multiple of 512
+  // every lane runs every iteration; only the loads' columns and the store are
+  // guarded when L is not a multiple of 512
   const int c0 = cb + lane * 8;
   const bool act = c0 < L;
   const int64_t col = act ? c0 : 0;
@@ -41,23 +41,23 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
       acc[2 * q + 1] += g * bf16_bits_to_f32(wv[q] >> 16);
     }
   };
-  int k = 0;
-  for (; k + 8 <= K; k += 8) {
+  // slots in batches of 8 loads in flight (the last batch guarded by a
+  // uniform test, so K = 22 is 3 round trips, not 2 plus 6 single loads); a
+  // slot's row and gate are read from its lane with readlane (no LDS trip)
+  for (int k = 0; k < K; k += 8) {
     u32x4 v[8];
     float g[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int r = __shfl(my_row, k + u, 64);
-      g[u] = __shfl(my_g, k + u, 64);
-      v[u] = *reinterpret_cast<const u32x4*>(y + (int64_t)r * L + col);
+      if (k + u < K) {
+        const int r = __builtin_amdgcn_readlane(my_row, k + u);
+        g[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), k + u));
+        v[u] = *reinterpret_cast<const u32x4*>(y + (int64_t)r * L + col);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) add(v[u], g[u]);     // slot order
-  }
-  for (; k < K; ++k) {
-    const int r = __shfl(my_row, k, 64);
-    const float g = __shfl(my_g, k, 64);
-    add(*reinterpret_cast<const u32x4*>(y + (int64_t)r * L + col), g);
+    for (int u = 0; u < 8; ++u)
+      if (k + u < K) add(v[u], g[u]);     // slot order
   }
   if (act) {
     const u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),

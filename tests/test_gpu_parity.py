@@ -93,6 +93,44 @@ def test_route_forced_bias():
     assert np.max(np.abs(gate - ref.gate) / ref.gate) < 1e-5
 
 
+def _bf16_grid(lo, hi):
+    """Every finite bf16 value in [lo, hi], as float32."""
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v)]
+    return np.unique(v[(v >= lo) & (v <= hi)])
+
+
+@pytest.mark.gpu
+def test_device_sigmoid_ulp_error():
+    """The router's fp32 sigmoid ([QA] Q5.2: sigmoid of the fp32 logits), read
+    back exactly: with two experts, K = 1, zero bias and the second expert's logit
+    at -200 (its fp32 sigmoid is 0), a token's routing gap c_(1) - c_(2) is the
+    first expert's sigmoid. Logits are every bf16 value in [-16, 16] (x carries
+    the logit, the weight row a 1; both products exact)."""
+    vals = _bf16_grid(-16.0, 16.0)
+    T, H = len(vals), 64
+    x = torch.zeros(T, H, dtype=torch.float32)
+    x[:, 0] = torch.from_numpy(vals)
+    x[:, 1] = 1.0
+    w = torch.zeros(2, H, dtype=torch.float32)
+    w[0, 0] = 1.0
+    w[1, 1] = -200.0
+    idx, gate, gap = M.route(x.to(torch.bfloat16).cuda(), w.cuda(), torch.zeros(2, device="cuda"), 1)
+    assert torch.all(idx == 0)
+    dev = gap.cpu().numpy().astype(np.float64)
+    ref = 1.0 / (1.0 + np.exp(-vals.astype(np.float64)))
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    err = np.abs(dev - ref) / ulp
+    worst = int(np.argmax(err))
+    log(f"[sigmoid] {T} logits in [-16, 16]: max error {err.max():.3f} ulp at l = {vals[worst]}, "
+        f"mean {err.mean():.3f} ulp")
+    # expf within 1 ulp, 1 + e and the division rounded: about 2 ulp of the
+    # result, in the finer ulp just below a power of two a little more
+    # (measured 1.98 at l = -0.003, sigmoid just below 1/2)
+    assert err.max() <= 2.5
+
+
 def test_route_ties_go_to_lower_index():
     d = dict(device_inputs("tiny"))
     wr = d["w_router"].clone()
