@@ -18,9 +18,11 @@
 //    line per tile; chunk c of row r sits in slot c ^ ((r >> 1) & 7), which
 //    keeps the ds_read_b128 fragment reads free of bank conflicts on gfx950's
 //    64-bank LDS;
-//  * two LDS stages; per k tile, one barrier, placed so that the loads of the
-//    next-but-one tile and the first fragment reads of the next tile overlap
-//    the MFMAs of the current tile's last substep.
+//  * two LDS stages of A and, in the 256x256 tiles, three of B (the weights,
+//    which the grouped products stream from HBM), so a B tile is loaded two k
+//    steps ahead; per k tile, one barrier, placed so that the loads of the
+//    next tiles and the first fragment reads of the next tile overlap the
+//    MFMAs of the current tile's last substep.
 // The 256x256 tile runs four waves of 128x128 each: a wave then reads half a
 // fragment per MFMA from LDS (a 128x64 wave tile reads three quarters), and
 // its 256 fp32 accumulators per lane live in AGPRs.
@@ -400,7 +402,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
     Frag f0, f1;
     // When each quarter of tile kt+2's loads is issued (plan digits for A lo, A hi,
     // B lo, B hi: 3 = after the barrier of step kt, 0 / 1 = in the first / second
-    // substep of step kt+1). All at the barrier left the waves' load issue in one
+    // substep of step kt+1; with three B stages the B quarters are tile kt+3's). All at the barrier left the waves' load issue in one
     // burst that put them out of step (the barrier then waits for the slowest):
     // spreading the B half over the next tile's first substeps took 3-6 % off
     // every product on the Ultra prefill, the best split differing by product.
