@@ -32,6 +32,10 @@ def _reference(d):
 @pytest.mark.parametrize("first,second", [
     (("tiny", {}), ("tiny", dict(T=37))),
     (("ultra_decode64", {}), ("ultra_decode1", {})),
+    # the tiled path: grouped products whose XCD tails are claimed through the
+    # counters in the scratch (zeroed by the permutation on every call), then a
+    # smaller tiled batch on the same scratch
+    (("tiny", dict(T=2048, H=512, L=256, E=32, I=1024, Is=512, K=4)), ("tiny", dict(T=300))),
 ])
 def test_noalloc_equals_forward_twice(first, second):
     for name, over in (first, second):
