@@ -635,7 +635,15 @@ gemm_bf16_kernel(const GemmLaunch L) {
     static_assert(WTMX * WTN * 2 <= ACH * 16 && WTMX * WTN * 2 <= BCH * 16, "staging fits a stage array");
     MOE_WAIT_VMCNT(0);
     __syncthreads();                               // all loads landed, all fragment reads done
-    char* stg = reinterpret_cast<char*>(wave == 0 ? sa0 : wave == 1 ? sb0 : wave == 2 ? sa1 : sb1);
+    constexpr int NWAVE = WM * WN;
+    static_assert(NWAVE <= 4 || (NWAVE == 8 && 2 * WTMX * WTN * 2 <= ACH * 16), "staging areas");
+    char* stg;
+    if constexpr (NWAVE <= 4) {
+      stg = reinterpret_cast<char*>(wave == 0 ? sa0 : wave == 1 ? sb0 : wave == 2 ? sa1 : sb1);
+    } else {                                       // eight waves: two wave tiles per stage array
+      const int h = wave >> 1;
+      stg = reinterpret_cast<char*>(h == 0 ? sa0 : h == 1 ? sb0 : h == 2 ? sa1 : sb1) + (wave & 1) * (WTMX * WTN * 2);
+    }
     const bool r2 = epi == EPI_RELU2_BF16;
 #pragma unroll
     for (int tm = 0; tm < TMX; ++tm) {

@@ -89,7 +89,7 @@ def _per_dispatch(counter_csv: str, counter: str):
 # step runs them (grouped launches carry their epilogue in the name)
 # (the few-token kernels: <slabs per wave, epilogue, weight format 0 bf16 / 1 MXFP8 / 3 MXFP4>)
 PHASE_KERNELS = {
-    "expert_up": (r"gemm_bf16_kernel<256, 256, 2, 2, 1, 1, 3>",) +
+    "expert_up": (r"gemm_bf16_kernel<256, 256, 2, 4, 1, 2, 3>",) +
                  tuple(f"skinny_kernel<{ns}, 1, {f}>" for ns in (1, 4) for f in (0, 1, 3)),
     "expert_down": (r"gemm_bf16_kernel<256, 256, 2, 2, 0, 1, 3>",) +
                    tuple(f"skinny_kernel<{ns}, 0, {f}>" for ns in (1, 4) for f in (0, 1, 3)),
