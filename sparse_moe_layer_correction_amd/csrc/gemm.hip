@@ -33,9 +33,10 @@ hipError_t launch_gemm(GemmLaunch& L, int cfg, hipStream_t st) {
     // k order per output, so the same bits) against four of 128x128, measured
     // on Ultra prefill, Nano and Super: 2-2.5 % faster for expert up and for
     // dense launches of up to 1536 tiles, 1-4 % slower for expert down and
-    // even or 1 % slower for the Ultra prefill's dense launches (2048-3072 tiles).
+    // even or 1 % slower for the Ultra prefill's dense launches (2048-3072 tiles)
+    // and 5 % slower for its router product (fp32 logits, 256 tiles).
     case TILE_256x256:
-      if (total < kDense8WaveMaxTiles)
+      if (total < kDense8WaveMaxTiles && L.p[0].epi != EPI_F32)
         hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, -1, 2, 3>), grid, dim3(512), 0, st, L);
       else
         hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, -1, 1, 3>), grid, dim3(256), 0, st, L);
