@@ -55,7 +55,8 @@ struct SkinnyProblem {
 };
 // the weight operand of a skinny product: bf16, MXFP8 or MXFP4 codes and scales, or fp32
 enum SkinnyBMode : int { kSkinnyBf16 = 0, kSkinnyMx = 1, kSkinnyF32 = 2, kSkinnyMx4 = 3 };
-hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st);
+// reduce = false: leave a split-K product's fp32 partials for the caller to sum
+hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st, bool reduce = true);
 // dense bf16 products of 1..16 rows, K split over the waves of a workgroup and
 // reduced in LDS (no partials, no second pass); P1: an optional second problem
 // in the same launch
@@ -83,6 +84,10 @@ hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* pa
 hipError_t launch_topk(const float* logits, const float* logits2, int64_t ldl, int nparts, int64_t part_off,
                        const float* bias, int T, int E, int K,
                        float scale, int n_group, int topk_group, int32_t* idx, float* gate, float* gap, hipStream_t st);
+// top-K from a few-token router product's split-K partials [ksplit, T, ldl], summed in split order
+hipError_t launch_topk_partials(const float* partial, int ksplit, int T, int64_t ldl, const float* bias, int E, int K,
+                                float scale, int n_group, int topk_group, int32_t* idx, float* gate, float* gap,
+                                hipStream_t st);
 hipError_t launch_permute_maps(const int32_t* idx, int T, int K, int E, int BM, const PermuteScratch& ps,
                                int32_t* offsets, int32_t* row_token, int32_t* slot_row, hipStream_t st);
 // n_valid: device scalar, the number of rows the maps filled (offsets[E]); rows past it are zeroed

@@ -278,11 +278,13 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int64_t EH = (int64_t)d.E * d.H;
   if (mk.mark(MOE_PHASE_ROUTER_GEMM) != hipSuccess) return MOE_ERR_HIP;
+  int fused_ksplit = 0;                      // > 0: the top-K sums the product's partials itself
   if (skinny) {
     SkinnyProblem P = skinny_dense(d.T, (int)l.ldl, d.E, logits, l.ldl, EPI_F32, d.H, partial, true);
     add_seg(P, x, d.H, nullptr, d.H, d.H);
     P.f32_b = w_router;
-    e = launch_skinny(P, st);
+    if (P.partial != nullptr) fused_ksplit = P.ksplit;
+    e = launch_skinny(P, st, fused_ksplit == 0);
   } else if (router_splits_k(d.T, d.H)) {
     // Many tokens: K split in two (each half of H over the three weight parts)
     // so that more tiles fill the CUs (E = 512 columns make only 2 column
@@ -318,9 +320,12 @@ int run_route(const moe_dims& d, const Layout& l, const uint16_t* x, const float
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (mk.mark(MOE_PHASE_TOPK) != hipSuccess) return MOE_ERR_HIP;
-  // (stacked weight parts lie E columns apart in a logit row)
-  e = launch_topk(logits, logits2, ldl, nparts, d.E, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d),
-                  topk_groups_of(d), idx, gate, gap, st);
+  if (fused_ksplit > 0)
+    e = launch_topk_partials(partial, fused_ksplit, d.T, l.ldl, bias, d.E, d.K, d.routed_scaling, groups_of(d),
+                             topk_groups_of(d), idx, gate, gap, st);
+  else  // (stacked weight parts lie E columns apart in a logit row)
+    e = launch_topk(logits, logits2, ldl, nparts, d.E, bias, d.T, d.E, d.K, d.routed_scaling, groups_of(d),
+                    topk_groups_of(d), idx, gate, gap, st);
   return hip_status(e);
 }
 

@@ -52,22 +52,15 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Top-K of token t by one wavefront from its logit row lrow (plus lrow2, the
+// other half of a K split, when not null).
 template <int VPL>
-__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
-                                                   const float* __restrict__ logits2, int64_t ldl,
-                                                   int nparts, int64_t part_off,
-                                                   const float* __restrict__ bias, int T, int E, int K,
-                                                   float scale, int n_group, int topk_group,
-                                                   int32_t* __restrict__ idx, float* __restrict__ gate,
-                                                   float* __restrict__ gap) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-
+__device__ __forceinline__ void topk_token(int t, int lane, const float* lrow, const float* lrow2, int nparts,
+                                           int64_t part_off, const float* __restrict__ bias, int E, int K,
+                                           float scale, int n_group, int topk_group, int32_t* __restrict__ idx,
+                                           float* __restrict__ gate, float* __restrict__ gap) {
   float s[VPL];
   uint64_t key[VPL];
-  const float* lrow = logits + (int64_t)t * ldl;
-  const float* lrow2 = logits2 ? logits2 + (int64_t)t * ldl : nullptr;   // the other half of a K split
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int e = j * 64 + lane;
@@ -202,6 +195,72 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   if (gap != nullptr && lane == 0) gap[t] = gapv;
 }
 
+template <int VPL>
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
+                                                   const float* __restrict__ logits2, int64_t ldl,
+                                                   int nparts, int64_t part_off,
+                                                   const float* __restrict__ bias, int T, int E, int K,
+                                                   float scale, int n_group, int topk_group,
+                                                   int32_t* __restrict__ idx, float* __restrict__ gate,
+                                                   float* __restrict__ gap) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token<VPL>(t, threadIdx.x & 63, logits + (int64_t)t * ldl, logits2 ? logits2 + (int64_t)t * ldl : nullptr,
+                  nparts, part_off, bias, E, K, scale, n_group, topk_group, idx, gate, gap);
+}
+
+// A few-token forward's router product leaves fp32 partial logits of ksplit
+// k ranges, [ksplit, T, ldl] (ldl a multiple of 64). One workgroup per token
+// sums its row into LDS and wave 0 takes the top-K from there: one launch
+// instead of a reduction pass and a top-K. A thread holds 4 experts; the
+// threads that cover the row form a team, and the teams sum consecutive
+// ranges of splits side by side (each split row read whole by a wave: 1 KB
+// per load, 8 loads in flight), after which the team sums are added in team
+// order. The order is fixed, so the logits do not change from call to call.
+constexpr int kPartThreads = 512;
+
+template <int VPL>
+__global__ void __launch_bounds__(kPartThreads) topk_partials_kernel(const float* __restrict__ partial, int ksplit,
+                                                                     int T, int64_t ldl,
+                                                                     const float* __restrict__ bias, int E, int K,
+                                                                     float scale, int n_group, int topk_group,
+                                                                     int32_t* __restrict__ idx,
+                                                                     float* __restrict__ gate,
+                                                                     float* __restrict__ gap) {
+  __shared__ float lg[64 * VPL];
+  __shared__ f32x4 team_sum[kPartThreads];
+  const int t = blockIdx.x;
+  const int64_t stride = (int64_t)T * ldl;
+  const int nq = (E + 3) >> 2;                       // 4-expert groups of the row
+  const int span = (nq + 63) & ~63;                  // a team: whole waves, <= 256 threads (E <= 1024)
+  const int teams = kPartThreads / span;             // 2, 4 or 8
+  const int team = threadIdx.x / span, q = threadIdx.x % span;
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (q < nq) {
+    const int k0 = (int)((int64_t)ksplit * team / teams), k1 = (int)((int64_t)ksplit * (team + 1) / teams);
+    const float* pq = partial + (int64_t)t * ldl + q * 4;
+    int k = k0;
+    for (; k + 8 <= k1; k += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(pq + (int64_t)(k + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; k < k1; ++k) s += *reinterpret_cast<const f32x4*>(pq + (int64_t)k * stride);
+  }
+  team_sum[threadIdx.x] = s;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kPartThreads) {
+    float v = team_sum[e >> 2][e & 3];
+    for (int m = 1; m < teams; ++m) v += team_sum[m * span + (e >> 2)][e & 3];
+    lg[e] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  topk_token<VPL>(t, threadIdx.x, lg, nullptr, 1, 0, bias, E, K, scale, n_group, topk_group, idx, gate, gap);
+}
+
 hipError_t launch_split_router_weight(const float* w, int E, int H, uint16_t* parts, hipStream_t st) {
   const int64_t n = (int64_t)E * H;
   int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
@@ -218,6 +277,22 @@ hipError_t launch_topk(const float* logits, const float* logits2, int64_t ldl, i
 #define MOE_TOPK(V)                                                                                           \
   hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, st, logits, logits2, ldl, nparts, part_off, bias, T, E, K, scale, n_group,   \
                      topk_group, idx, gate, gap)
+  if (vpl <= 1) MOE_TOPK(1);
+  else if (vpl <= 2) MOE_TOPK(2);
+  else if (vpl <= 4) MOE_TOPK(4);
+  else if (vpl <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_partials(const float* partial, int ksplit, int T, int64_t ldl, const float* bias, int E, int K,
+                                float scale, int n_group, int topk_group, int32_t* idx, float* gate, float* gap,
+                                hipStream_t st) {
+  const int vpl = (E + 63) / 64;
+#define MOE_TOPK(V)                                                                                            \
+  hipLaunchKernelGGL(topk_partials_kernel<V>, dim3(T), dim3(kPartThreads), 0, st, partial, ksplit, T, ldl, bias, E, K, scale, \
+                     n_group, topk_group, idx, gate, gap)
   if (vpl <= 1) MOE_TOPK(1);
   else if (vpl <= 2) MOE_TOPK(2);
   else if (vpl <= 4) MOE_TOPK(4);

@@ -779,7 +779,7 @@ __global__ void __launch_bounds__(256) skinny_reduce_wide_kernel(const float* __
   }
 }
 
-hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
+hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st, bool reduce) {
   // dense products carry up to 64 rows: 4 slabs per wave load the rows once per
   // four weight fragments; grouped products have a few rows per expert
   const int nsb = skinny_slabs_per_wave(P);
@@ -826,7 +826,7 @@ hipError_t launch_skinny(const SkinnyProblem& P, hipStream_t st) {
 #undef MOE_GROUPED_MX
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || P.partial == nullptr) return e;
+  if (e != hipSuccess || P.partial == nullptr || !reduce) return e;
   const int64_t total = (int64_t)P.M * P.N;
   if (P.ksplit >= 16 && total / 4 <= 4096)
     hipLaunchKernelGGL(skinny_reduce_wide_kernel, dim3((unsigned)((total / 4 + 3) / 4)), dim3(256), 0, st, P.partial,
