@@ -96,6 +96,39 @@ __device__ __forceinline__ void tile_order(int t, int mtiles, int ntiles, int gm
   nt = rem / gm;
 }
 
+// Order of a grouped expert's tiles. An XCD hands its workgroups, in order, to
+// its four shader engines in turn (measured: every fourth workgroup goes to the
+// same engine whatever its tile costs, and the hand-out waits for the engine
+// whose turn it is). With the short last M tile of an expert next to its full
+// ones, tiles of one height went to the same engines (two M tiles per expert:
+// two engines had only full tiles, two only short ones). So the N tiles go in
+// blocks (all of them up to 8, else 4 at a time): a block holds first the
+// expert's full-height M tiles for its N tiles (rasters of gm_ M tiles, M
+// fastest in a raster, so that the M tiles sharing a weight panel run side by
+// side), then the short M tile for the same N tiles; with a multiple of 4 N
+// tiles every run of one tile height is a multiple of 4 long and each engine
+// gets the same mix. (Blocks of 4 out of 8 N tiles made an M tile's rows be
+// read again half an expert later: Super's 31-tile expert, expert down +1.4 %.)
+// ne M tiles, the first nfull of full height.
+__host__ __device__ __forceinline__ void grouped_tile_order(int local, int ne, int nfull, int ntl, int gm_, int& mt,
+                                                            int& nt) {
+  const int PB = ntl <= 8 ? ntl : 4;
+  const int blk = local / (ne * PB);
+  const int nb = min(PB, ntl - blk * PB);
+  const int rem = local - blk * ne * PB;
+  if (rem < nfull * nb) {
+    const int per = gm_ * nb;
+    const int g = rem / per;
+    const int gm = min(gm_, nfull - g * gm_);
+    const int r2 = rem - g * per;
+    mt = g * gm_ + r2 % gm;
+    nt = blk * PB + r2 / gm;
+  } else {
+    mt = ne - 1;
+    nt = blk * PB + (rem - nfull * nb);
+  }
+}
+
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
@@ -245,9 +278,8 @@ gemm_bf16_kernel(const GemmLaunch L) {
     const int e = info.x, f = info.y, o0 = info.z, o1 = info.w;
     const int ne = (o1 - o0 + BM - 1) / BM;
     const int local = t - f * ntl;
-    // inside an expert, rasters of group_m M tiles (M fastest in a group)
     int mt, nt;
-    tile_order(local, ne, ntl, L.p[0].group_m, mt, nt);
+    grouped_tile_order(local, ne, (o1 - o0) / BM, ntl, L.p[0].group_m, mt, nt);
     m0 = o0 + mt * BM;
     mend = o1;
     n0 = nt * BN;
