@@ -710,20 +710,23 @@ gemm_bf16_kernel(const GemmLaunch L) {
       const int c = lane % CPW;
       rb[i] = *reinterpret_cast<const u32x4*>(stg + r * (CPW * 16) + ((c ^ (r % CPW)) * 16));
     }
+    // read-back i holds row mfirst + i * RPI of the output at columns n..n+7:
+    // the row offsets advance by a fixed stride, and the column tests hold for
+    // every row (per row, the 64-bit row products and the tests had cost about
+    // 20 instructions per store)
+    const int mfirst = m0 + wave_m * WTMX + lane / CPW;
+    const int n = n0 + wave_n * WTN + (lane % CPW) * 8;
+    const bool cols = n < Nc, full = n + 8 <= Nc;    // else 4 columns (N is a multiple of 4)
+    int64_t doff = (int64_t)mfirst * ldc + n, soff = (int64_t)mfirst * ldr + n;
+    const int64_t dstep = (int64_t)RPI * ldc, sstep = (int64_t)RPI * ldr;
 #pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-      const int r = i * RPI + lane / CPW;
-      const int c = lane % CPW;
+    for (int i = 0; i < NRB; ++i, doff += dstep, soff += sstep) {
+      if (!cols || mfirst + i * RPI >= mend) continue;
       const u32x4 v = rb[i];
-      const int m = m0 + wave_m * WTMX + r;
-      const int n = n0 + wave_n * WTN + c * 8;
-      if (m >= mend || n >= Nc) continue;
-      uint16_t* dst = Cp + (int64_t)m * ldc + n;
-      const bool full = n + 8 <= Nc;                  // else 4 columns (N is a multiple of 4)
       u32x4 o = v;
       if (EPI < 0 && res != nullptr) {
         // the block's residual add: bf16 + bf16 in fp32 (exact), rounded once
-        const uint16_t* src = res + (int64_t)m * ldr + n;
+        const uint16_t* src = res + soff;
         u32x4 rv;
         if (full) rv = *reinterpret_cast<const u32x4*>(src);
         else {
@@ -735,6 +738,7 @@ gemm_bf16_kernel(const GemmLaunch L) {
           o[q] = cvt_pk_bf16(bf16_bits_to_f32(v[q] & 0xFFFFu) + bf16_bits_to_f32(rv[q] & 0xFFFFu),
                              bf16_bits_to_f32(v[q] >> 16) + bf16_bits_to_f32(rv[q] >> 16));
       }
+      uint16_t* dst = Cp + doff;
       if (full) *reinterpret_cast<u32x4*>(dst) = o;
       else *reinterpret_cast<u32x2*>(dst) = u32x2{o[0], o[1]};
     }
